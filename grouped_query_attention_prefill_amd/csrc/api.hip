@@ -1,0 +1,173 @@
+// C ABI of the grouped-query attention library: argument validation and
+// dispatch to the kernels.  Every host-checkable error is reported before any
+// launch; nothing is allocated and no state is kept between calls.
+#include "gqa.h"
+#include "internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+using gqa::AttnArgs;
+using gqa::DecodeArgs;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// dtype/d_h combinations with a kernel behind them
+int check_types(int in_dtype, int out_dtype, int d_h) {
+  if (in_dtype == GQA_F32) {
+    if (out_dtype != GQA_F32) return GQA_ERR_UNSUPPORTED;
+    if (d_h < 1 || d_h > 256) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+  }
+  if (in_dtype == GQA_BF16) {
+    if (out_dtype != GQA_F32 && out_dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+    if (d_h != 64 && d_h != 128) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+  }
+  return GQA_ERR_UNSUPPORTED;
+}
+
+bool known_dtype(int t) { return t == GQA_F32 || t == GQA_BF16; }
+
+int check_ptrs(int in_dtype, int out_dtype, const void* q, const void* k, const void* v, const void* o) {
+  if (!q || !k || !v || !o) return GQA_ERR_INVALID_ARGUMENT;
+  const uintptr_t in_al = in_dtype == GQA_BF16 ? 16 : 4;
+  const uintptr_t out_al = in_dtype == GQA_BF16 ? (out_dtype == GQA_BF16 ? 8 : 16) : 4;
+  if (!aligned(q, in_al) || !aligned(k, in_al) || !aligned(v, in_al) || !aligned(o, out_al))
+    return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
+
+int run_attention(const AttnArgs& a, int in_dtype, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.B == 0) return GQA_OK;
+  hipError_t e = in_dtype == GQA_F32 ? gqa::launch_attn_f32(a, s) : gqa::launch_attn_bf16(a, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,
+                      int B, int h_q, int h_kv, int S_q, int T_cap, int d_h,
+                      int mask, const int32_t* kv_lens, const int32_t* q_pos0,
+                      float scale, int in_dtype, int out_dtype, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || S_q < 1 || T_cap < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (mask != GQA_MASK_NONE && mask != GQA_MASK_CAUSAL) return GQA_ERR_INVALID_ARGUMENT;
+  if (!scale_ok(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  int st = check_types(in_dtype, out_dtype, d_h);
+  if (st != GQA_OK) return st;
+  st = check_ptrs(in_dtype, out_dtype, q, k_cache, v_cache, o);
+  if (st != GQA_OK) return st;
+  if ((kv_lens && !aligned(kv_lens, 4)) || (q_pos0 && !aligned(q_pos0, 4))) return GQA_ERR_INVALID_ARGUMENT;
+  AttnArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o;
+  a.kv_lens = kv_lens; a.q_pos0 = q_pos0;
+  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.S_q = S_q; a.T_cap = T_cap; a.D = d_h;
+  a.causal = mask == GQA_MASK_CAUSAL ? 1 : 0;
+  a.q_pos_from_end = 1;
+  a.scale = scale;
+  a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
+  return run_attention(a, in_dtype, stream);
+}
+
+int gqa_prefill(const void* q, const void* k, const void* v, void* o,
+                int B, int h_q, int h_kv, int T, int d_h,
+                int mask, const int32_t* kv_lens, float scale,
+                int in_dtype, int out_dtype, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || T < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (mask != GQA_MASK_NONE && mask != GQA_MASK_CAUSAL) return GQA_ERR_INVALID_ARGUMENT;
+  if (!scale_ok(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  int st = check_types(in_dtype, out_dtype, d_h);
+  if (st != GQA_OK) return st;
+  st = check_ptrs(in_dtype, out_dtype, q, k, v, o);
+  if (st != GQA_OK) return st;
+  if (kv_lens && !aligned(kv_lens, 4)) return GQA_ERR_INVALID_ARGUMENT;
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.kv_lens = kv_lens; a.q_pos0 = nullptr;
+  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.S_q = T; a.T_cap = T; a.D = d_h;
+  a.causal = mask == GQA_MASK_CAUSAL ? 1 : 0;
+  a.q_pos_from_end = 0;    // query i sits at position i
+  a.scale = scale;
+  a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
+  return run_attention(a, in_dtype, stream);
+}
+
+size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int T_cap, int d_h, int in_dtype) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || T_cap < 1 || d_h < 1 || h_q % h_kv != 0) return 0;
+  if (in_dtype != GQA_BF16) return 0;
+  if (d_h != 64 && d_h != 128) return 0;
+  return gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, T_cap).workspace_bytes;
+}
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* seq_lens, const int32_t* q_pos, void* o,
+               int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+               float scale, int in_dtype, int out_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || T_cap < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (max_seq_len > T_cap) return GQA_ERR_INVALID_ARGUMENT;
+  if (!scale_ok(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  int st = check_types(in_dtype, out_dtype, d_h);
+  if (st != GQA_OK) return st;
+  st = check_ptrs(in_dtype, out_dtype, q, k_cache, v_cache, o);
+  if (st != GQA_OK) return st;
+  if (!seq_lens || !aligned(seq_lens, 4) || (q_pos && !aligned(q_pos, 4))) return GQA_ERR_INVALID_ARGUMENT;
+  const int len = max_seq_len > 0 ? max_seq_len : T_cap;
+  DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.q_pos = q_pos; a.o = o;
+  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.T_cap = T_cap; a.D = d_h; a.max_len = len;
+  a.scale = scale;
+  a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (in_dtype == GQA_F32) return hip_status(gqa::launch_decode_f32(a, s));
+  const gqa::DecodePlan pl = gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, len);
+  if (pl.n_split > 1) {
+    if (workspace_bytes < pl.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned(workspace, 16)) return GQA_ERR_INVALID_ARGUMENT;
+  }
+  return hip_status(gqa::launch_decode_bf16(a, pl, s));
+}
+
+int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h,
+                  int dtype, void* stream) {
+  if (B < 1 || h_kv < 1 || T_cap < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!k_cache || !v_cache || !k_new || !v_new || !write_pos) return GQA_ERR_INVALID_ARGUMENT;
+  const int eb = dtype == GQA_BF16 ? 2 : 4;
+  const uintptr_t al = (d_h * eb) % 16 == 0 ? 16 : (uintptr_t)eb;
+  if (!aligned(k_cache, al) || !aligned(v_cache, al) || !aligned(k_new, al) || !aligned(v_new, al) ||
+      !aligned(write_pos, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  return hip_status(gqa::launch_kv_append(k_cache, v_cache, k_new, v_new, write_pos, B, h_kv, T_cap,
+                                          d_h, eb, static_cast<hipStream_t>(stream)));
+}
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK: success";
+    case GQA_ERR_INVALID_ARGUMENT: return "GQA_ERR_INVALID_ARGUMENT: invalid size, pointer, mask or scale";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: unsupported dtype / head-width combination";
+    case GQA_ERR_WORKSPACE_TOO_SMALL: return "GQA_ERR_WORKSPACE_TOO_SMALL: decode workspace below gqa_decode_workspace_bytes()";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP: HIP launch failure";
+    default: return "unknown gqa status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace gqa {
+
+// Attention over a cache for S_q query rows per sequence at absolute positions
+// q_pos0[b] + i.  Prefill is the case q_pos0 = 0, S_q = T_cap.
+struct AttnArgs {
+  const void* q;          // (B, h_q, S_q, D)
+  const void* k;          // (B, h_kv, T_cap, D)
+  const void* v;          // (B, h_kv, T_cap, D)
+  void* o;                // (B, h_q, S_q, D)
+  const int32_t* kv_lens; // (B,) or null -> T_cap
+  const int32_t* q_pos0;  // (B,) or null -> (kv_len - S_q) when from_end, else 0
+  int B, h_q, h_kv, S_q, T_cap, D;
+  int causal;
+  int q_pos_from_end;     // 1: default position of row 0 is kv_len - S_q
+  float scale;
+  int out_bf16;           // output dtype of the bf16 path
+};
+
+// Decode: one query per sequence at q_pos[b] (null -> seq_lens[b] - 1), keys
+// j < min(seq_lens[b], q_pos[b] + 1, max_len).
+struct DecodeArgs {
+  const void* q;          // (B, h_q, 1, D)
+  const void* k;          // (B, h_kv, T_cap, D)
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* q_pos;
+  void* o;                // (B, h_q, 1, D)
+  int B, h_q, h_kv, T_cap, D, max_len;
+  float scale;
+  int out_bf16;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+struct DecodePlan {
+  int head_chunks;   // ceil(r / 32)
+  int chunk;         // keys per split (multiple of the key tile)
+  int n_split;       // splits launched
+  int n_split_cap;   // splits the workspace is sized for
+  size_t workspace_bytes;
+};
+
+// Split plan for the bf16 decode path.  `len` is the grid-sizing bound.
+DecodePlan plan_decode_bf16(int B, int h_q, int h_kv, int T_cap, int D, int len);
+
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* write_pos, int B, int h_kv, int T_cap, int D,
+                            int elem_bytes, hipStream_t s);
+
+}  // namespace gqa

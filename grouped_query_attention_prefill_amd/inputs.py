@@ -5,11 +5,11 @@ out.  Both the HIP path and the CPU oracle consume what it returns, so it
 imports neither of them.
 
 Recipe (the same for every workload):
-  * ``numpy.random.Generator(PCG64(seed))``; one generator per workload;
-  * draw order: per-sequence lengths (ragged workload only), then Q, then K,
-    then V, then the appended token's K and V;
-  * each tensor is drawn one batch row at a time with
-    ``standard_normal(dtype=float32)`` (bounded host memory), i.e. N(0, 1);
+  * numpy PCG64 streams keyed by ``SeedSequence(seed, spawn_key=(tensor, row))``:
+    one independent stream per tensor and per batch row, so rows can be drawn
+    in parallel threads and any row can be regenerated on its own;
+    tensor ids: Q 0, K 1, V 2, appended K 3, appended V 4, lengths 5 (one stream);
+  * values are ``standard_normal(dtype=float32)``, i.e. N(0, 1);
   * bf16 tensors are those float32 draws rounded to bf16, round-to-nearest-even;
     both sides see exactly those bf16 values (the oracle widens them to float64
     exactly);
@@ -24,7 +24,9 @@ bf16 tensors are returned as ``uint16`` bit patterns, float32 tensors as
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -33,8 +35,19 @@ SEED_BASE = 1949
 BF16_QNAN = np.uint16(0x7FC0)
 
 
-def rng_for(seed: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(seed))
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "k_new": 3, "v_new": 4, "lengths": 5}
+
+
+def rng_for(seed: int, tensor: int = 5, row: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tensor, row))))
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -53,28 +66,32 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    """N(0,1) tensor drawn one leading-index slice at a time.
+def normal(seed: int, tensor: str, shape, dtype: str, rows=None) -> np.ndarray:
+    """N(0,1) tensor; leading index b is drawn from stream (seed, tensor, b).
 
     dtype "f32" -> float32 array; "bf16" -> uint16 bf16 bit patterns.
+    ``rows`` restricts the draw to those leading indices (others stay zero).
     """
     shape = tuple(int(s) for s in shape)
-    if dtype == "f32":
-        out = np.empty(shape, dtype=np.float32)
-    elif dtype == "bf16":
-        out = np.empty(shape, dtype=np.uint16)
-    else:
+    out = np.zeros(shape, dtype=np.float32 if dtype == "f32" else np.uint16)
+    if dtype not in ("f32", "bf16"):
         raise ValueError(f"unknown dtype {dtype}")
     if len(shape) == 0 or shape[0] == 0:
         return out
-    for i in range(shape[0]):
-        x = rng.standard_normal(shape[1:], dtype=np.float32)
+    tid = TENSOR_IDS[tensor]
+
+    def fill(i):
+        x = rng_for(seed, tid, i).standard_normal(shape[1:], dtype=np.float32)
         out[i] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    idx = range(shape[0]) if rows is None else rows
+    with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, idx))
     return out
 
 
-def ragged_lengths(rng: np.random.Generator, B: int, lo: int = 1, hi: int = 32768) -> np.ndarray:
-    return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+def ragged_lengths(seed: int, B: int, lo: int = 1, hi: int = 32768) -> np.ndarray:
+    return rng_for(seed, TENSOR_IDS["lengths"]).integers(lo, hi, size=B, endpoint=True).astype(np.int32)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -117,10 +134,9 @@ WORKLOADS = {
 
 def make_prefill(B, h_q, h_kv, d_h, T, dtype, seed, kv_lens: Optional[np.ndarray] = None):
     """Q (B,h_q,T,d_h), K, V (B,h_kv,T,d_h).  Returns a dict of host arrays."""
-    rng = rng_for(seed)
-    q = normal(rng, (B, h_q, T, d_h), dtype)
-    k = normal(rng, (B, h_kv, T, d_h), dtype)
-    v = normal(rng, (B, h_kv, T, d_h), dtype)
+    q = normal(seed, "q", (B, h_q, T, d_h), dtype)
+    k = normal(seed, "k", (B, h_kv, T, d_h), dtype)
+    v = normal(seed, "v", (B, h_kv, T, d_h), dtype)
     d = {"q": q, "k": k, "v": v}
     if kv_lens is not None:
         d["kv_lens"] = np.asarray(kv_lens, dtype=np.int32)
@@ -133,10 +149,9 @@ def make_decode(B, h_q, h_kv, d_h, T_cap, dtype, seed, seq_lens=None, poison=Fal
     seq_lens defaults to T_cap for every sequence (full cache, query at T_cap-1).
     With ``poison``, cache rows >= seq_lens[b] are set to NaN.
     """
-    rng = rng_for(seed)
-    q = normal(rng, (B, h_q, 1, d_h), dtype)
-    k = normal(rng, (B, h_kv, T_cap, d_h), dtype)
-    v = normal(rng, (B, h_kv, T_cap, d_h), dtype)
+    q = normal(seed, "q", (B, h_q, 1, d_h), dtype)
+    k = normal(seed, "k", (B, h_kv, T_cap, d_h), dtype)
+    v = normal(seed, "v", (B, h_kv, T_cap, d_h), dtype)
     lens = np.full(B, T_cap, np.int32) if seq_lens is None else np.asarray(seq_lens, np.int32)
     if poison:
         _poison_rows(k, lens, dtype)
@@ -152,15 +167,14 @@ def make_append_decode(B, h_q, h_kv, d_h, T_cap, dtype, seed, hist_hi, lens=None
     at absolute position hist[b].  Rows >= hist[b] are NaN before the append (row
     hist[b] is then overwritten by the append), rows > hist[b] stay NaN.
     """
-    rng = rng_for(seed)
-    hist = ragged_lengths(rng, B, 1, hist_hi) if lens is None else np.asarray(lens, np.int32)
+    hist = ragged_lengths(seed, B, 1, hist_hi) if lens is None else np.asarray(lens, np.int32)
     if int(hist.max()) + 1 > T_cap:
         raise ValueError("cache capacity too small for the drawn lengths")
-    q = normal(rng, (B, h_q, 1, d_h), dtype)
-    k = normal(rng, (B, h_kv, T_cap, d_h), dtype)
-    v = normal(rng, (B, h_kv, T_cap, d_h), dtype)
-    k_new = normal(rng, (B, h_kv, 1, d_h), dtype)
-    v_new = normal(rng, (B, h_kv, 1, d_h), dtype)
+    q = normal(seed, "q", (B, h_q, 1, d_h), dtype)
+    k = normal(seed, "k", (B, h_kv, T_cap, d_h), dtype)
+    v = normal(seed, "v", (B, h_kv, T_cap, d_h), dtype)
+    k_new = normal(seed, "k_new", (B, h_kv, 1, d_h), dtype)
+    v_new = normal(seed, "v_new", (B, h_kv, 1, d_h), dtype)
     _poison_rows(k, hist, dtype)
     _poison_rows(v, hist, dtype)
     return {

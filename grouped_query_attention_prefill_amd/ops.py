@@ -1,0 +1,247 @@
+"""Thin ctypes binding of libgqa.so with the C entry points' names.
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind the C ABI (``include/gqa.h``).  PyTorch provides device memory
+(``torch.empty``) and the current stream; nothing here computes attention.
+The library must be built (``python -m grouped_query_attention_prefill_amd.build``);
+loading fails loudly otherwise -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgqa.so")
+
+GQA_OK = 0
+GQA_ERR_INVALID_ARGUMENT = 1
+GQA_ERR_UNSUPPORTED = 2
+GQA_ERR_WORKSPACE_TOO_SMALL = 3
+GQA_ERR_HIP = 4
+GQA_F32 = 0
+GQA_BF16 = 1
+GQA_MASK_NONE = 0
+GQA_MASK_CAUSAL = 1
+
+# exported symbol -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+SIGNATURES = {
+    "gqa_prefill": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P]),
+    "gqa_prefill_chunk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _F, _I, _I, _P]),
+    "gqa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
+    "gqa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
+    "gqa_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "gqa_status_string": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(gqa_status_string(status))
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgqa.so and declare its prototypes.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m grouped_query_attention_prefill_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def gqa_status_string(status: int) -> str:
+    return load_library().gqa_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != GQA_OK:
+        raise GQAError(status)
+
+
+# ------------------------------------------------------------------ torch marshalling helpers
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return GQA_F32
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return torch.float32 if code == GQA_F32 else torch.bfloat16
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_tensor(t, name, dims=None):
+    _require(t.is_cuda, f"{name} must be a device tensor")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+    if dims is not None:
+        _require(t.dim() == dims, f"{name} must be {dims}-D")
+
+
+def _int_vec(t, name, B, device):
+    if t is None:
+        return None
+    torch = _torch()
+    _dev_tensor(t, name, 1)
+    _require(t.dtype == torch.int32 and t.numel() == B, f"{name} must be int32 of shape ({B},)")
+    _require(t.device == device, f"{name} must be on {device}")
+    return t
+
+
+def _out_code(in_code: int, out_dtype) -> int:
+    if out_dtype is None:
+        return GQA_F32
+    torch = _torch()
+    return GQA_F32 if out_dtype == torch.float32 else GQA_BF16
+
+
+# ------------------------------------------------------------------ entry points
+def gqa_prefill(q, k, v, *, causal: bool = True, scale: Optional[float] = None, kv_lens=None,
+                out=None, out_dtype=None):
+    """O = grouped-query attention of q (B,h_q,T,d_h) over k, v (B,h_kv,T,d_h).
+
+    Returns ``out`` (allocated with ``torch.empty`` when None); fp32 output by default.
+    """
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, n, 4)
+    B, h_q, T, d_h = q.shape
+    _require(k.shape == v.shape and k.shape[0] == B and k.shape[2] == T and k.shape[3] == d_h,
+             "k, v must be (B, h_kv, T, d_h) matching q")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    h_kv = k.shape[1]
+    code = _dtype_code(q)
+    oc = _out_code(code, out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((B, h_q, T, d_h), dtype=_torch_dtype(oc), device=q.device)
+    _dev_tensor(out, "out", 4)
+    _require(tuple(out.shape) == (B, h_q, T, d_h), "out must be (B, h_q, T, d_h)")
+    kv_lens = _int_vec(kv_lens, "kv_lens", B, q.device)
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    lib = load_library()
+    _check(lib.gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h_q, h_kv, T, d_h,
+                           GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc,
+                           code, oc, _stream_handle(q.device)))
+    return out
+
+
+def gqa_prefill_chunk(q, k_cache, v_cache, *, kv_lens=None, q_pos0=None, causal: bool = True,
+                      scale: Optional[float] = None, out=None, out_dtype=None):
+    """S_q queries per sequence at absolute positions q_pos0[b] + i against a cache."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, n, 4)
+    B, h_q, S_q, d_h = q.shape
+    _require(k_cache.shape == v_cache.shape and k_cache.shape[0] == B and k_cache.shape[3] == d_h,
+             "caches must be (B, h_kv, T_cap, d_h)")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q and caches must share a dtype")
+    h_kv, T_cap = k_cache.shape[1], k_cache.shape[2]
+    code = _dtype_code(q)
+    oc = _out_code(code, out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((B, h_q, S_q, d_h), dtype=_torch_dtype(oc), device=q.device)
+    _dev_tensor(out, "out", 4)
+    _require(tuple(out.shape) == (B, h_q, S_q, d_h), "out must be (B, h_q, S_q, d_h)")
+    kv_lens = _int_vec(kv_lens, "kv_lens", B, q.device)
+    q_pos0 = _int_vec(q_pos0, "q_pos0", B, q.device)
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    lib = load_library()
+    _check(lib.gqa_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, h_q, h_kv, S_q,
+                                 T_cap, d_h, GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens),
+                                 _ptr(q_pos0), sc, code, oc, _stream_handle(q.device)))
+    return out
+
+
+def gqa_decode_workspace_bytes(B: int, h_q: int, h_kv: int, T_cap: int, d_h: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(load_library().gqa_decode_workspace_bytes(B, h_q, h_kv, T_cap, d_h, code))
+
+
+def gqa_decode(q, k_cache, v_cache, seq_lens, *, q_pos=None, scale: Optional[float] = None,
+               max_seq_len: Optional[int] = None, out=None, out_dtype=None, workspace=None):
+    """One query per sequence, q (B,h_q,1,d_h), against caches (B,h_kv,T_cap,d_h)."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, n, 4)
+    B, h_q, S_q, d_h = q.shape
+    _require(S_q == 1, "decode takes one query per sequence (S_q = 1)")
+    _require(k_cache.shape == v_cache.shape and k_cache.shape[0] == B and k_cache.shape[3] == d_h,
+             "caches must be (B, h_kv, T_cap, d_h)")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q and caches must share a dtype")
+    h_kv, T_cap = k_cache.shape[1], k_cache.shape[2]
+    code = _dtype_code(q)
+    oc = _out_code(code, out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((B, h_q, 1, d_h), dtype=_torch_dtype(oc), device=q.device)
+    _dev_tensor(out, "out", 4)
+    _require(tuple(out.shape) == (B, h_q, 1, d_h), "out must be (B, h_q, 1, d_h)")
+    seq_lens = _int_vec(seq_lens, "seq_lens", B, q.device)
+    _require(seq_lens is not None, "seq_lens is required")
+    q_pos = _int_vec(q_pos, "q_pos", B, q.device)
+    lib = load_library()
+    ws_bytes = int(lib.gqa_decode_workspace_bytes(B, h_q, h_kv, T_cap, d_h, code))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    msl = 0 if max_seq_len is None else int(max_seq_len)
+    _check(lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(q_pos), _ptr(out),
+                          B, h_q, h_kv, T_cap, d_h, msl, sc, code, oc, _ptr(workspace), ws_have,
+                          _stream_handle(q.device)))
+    return out
+
+
+def gqa_kv_append(k_cache, v_cache, k_new, v_new, write_pos):
+    """Write k_new, v_new (B,h_kv,1,d_h) into row write_pos[b] of the caches (in place)."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, n, 4)
+    B, h_kv, T_cap, d_h = k_cache.shape
+    _require(v_cache.shape == k_cache.shape, "caches must match")
+    _require(tuple(k_new.shape) == (B, h_kv, 1, d_h) and k_new.shape == v_new.shape,
+             "k_new, v_new must be (B, h_kv, 1, d_h)")
+    _require(k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype, "dtypes must match")
+    write_pos = _int_vec(write_pos, "write_pos", B, k_cache.device)
+    _require(write_pos is not None, "write_pos is required")
+    lib = load_library()
+    _check(lib.gqa_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(write_pos),
+                             B, h_kv, T_cap, d_h, _dtype_code(k_cache), _stream_handle(k_cache.device)))
+    return k_cache, v_cache

@@ -1,0 +1,164 @@
+/*
+ * gqa.h -- C ABI of the grouped-query attention library for MI355X (gfx950).
+ *
+ * The library computes, for every sequence b and query head a,
+ *
+ *     O[b,a] = softmax( scale * Q[b,a] K[b,g(a)]^T + M ) V[b,g(a)],
+ *     g(a) = floor(a / r),  r = h_q / h_kv,
+ *
+ * which covers multi-head (h_kv = h_q), grouped-query (1 < h_kv < h_q) and
+ * multi-query (h_kv = 1) attention with one code path.  Sources (web pages):
+ *   [EffSeq]    "序列计算与存储", note.the0xka1.cc efficient-sequence-models:
+ *               section 分组查询注意力 (formula, group map, shapes, causal or
+ *               padding mask), 缓存字节 (cache layout (B, h_kv, T, d_h) read
+ *               through the group index, never duplicated), 在线 softmax
+ *               (running max, normalizer and unnormalized output).
+ *   [AttnVar]   "第三章：MHA 的局限与 MQA、GQA、Flash Attention", sections 3.1
+ *               (decode: the new token's K/V are appended, then all visible
+ *               K/V are read), 3.3 (is_causal only fits equal Q/K lengths),
+ *               3.5 (merging two partial softmax states).
+ *   [MhaMqaGqa] zane-jiang mha-mqa-gqa, sections 4 (KV cache), 7 (one K/V
+ *               tile serves all r query rows of its group), 9 (split the
+ *               history when rows are few).
+ *   [Ch09]      "第 09 章 GQA、MLA 与跨层 KV 共享", section 09.2 (absolute
+ *               query position in cached decoding; reset clears K, V and the
+ *               position together).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  Layouts are
+ *     dense row-major: Q and O are (B, h_q, S_q, d_h); K, V and the caches are
+ *     (B, h_kv, T, d_h).  Integer arrays are device int32.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream).  Calls return once enqueued.
+ *   - The library allocates no device memory and keeps no state between
+ *     calls; calls on different streams are independent.
+ *   - Host-checkable argument errors return a status before any launch and
+ *     leave every output untouched.  Launch failures return GQA_ERR_HIP.
+ *   - Data conditions that only the device can see have defined results:
+ *     lengths are clamped to [0, capacity]; a query row with no visible key
+ *     is written as zeros; cache rows a query cannot see are never used, so
+ *     they may hold any bits (NaN included).
+ *   - `scale` multiplies Q K^T; it must be finite and > 0 (the pages fix it at
+ *     1/sqrt(d_h); the Python binding passes that when given none).
+ *   - Supported: in_dtype GQA_F32 with out_dtype GQA_F32 for 1 <= d_h <= 256
+ *     (reference-precision path); in_dtype GQA_BF16 with out_dtype GQA_F32 or
+ *     GQA_BF16 for d_h in {64, 128} (matrix-core path, fp32 accumulation).
+ *     Anything else returns GQA_ERR_UNSUPPORTED.
+ *   - Alignment: bf16 tensors and fp32 outputs of the bf16 path need 16-byte
+ *     aligned base pointers; fp32 tensors need 4-byte alignment.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARGUMENT = 1,
+  GQA_ERR_UNSUPPORTED = 2,
+  GQA_ERR_WORKSPACE_TOO_SMALL = 3,
+  GQA_ERR_HIP = 4
+} gqa_status_t;
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype_t;
+
+typedef enum { GQA_MASK_NONE = 0, GQA_MASK_CAUSAL = 1 } gqa_mask_t;
+
+/*
+ * Prefill: S_q = T queries at positions 0..T-1 attend to T keys.
+ * Key j is visible to query i iff j < len_b and (mask == GQA_MASK_NONE or j <= i),
+ * with len_b = kv_lens[b] clamped to [0, T] (kv_lens == NULL: len_b = T).
+ * Causal masking is the [EffSeq] / [Ch09] 09.2 mask (-inf for j > i), applied
+ * by selection; padding follows the per-sequence-length reading of [EffSeq].
+ *
+ *   q  (B, h_q, T, d_h)  in_dtype      k, v (B, h_kv, T, d_h) in_dtype
+ *   o  (B, h_q, T, d_h)  out_dtype     kv_lens (B,) int32 or NULL
+ * Errors: GQA_ERR_INVALID_ARGUMENT for a size < 1, h_q % h_kv != 0, a NULL or
+ * misaligned tensor pointer, an unknown mask, a scale that is not finite and
+ * positive; GQA_ERR_UNSUPPORTED for an unsupported dtype / d_h combination.
+ */
+int gqa_prefill(const void* q, const void* k, const void* v, void* o,
+                int B, int h_q, int h_kv, int T, int d_h,
+                int mask, const int32_t* kv_lens, float scale,
+                int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Chunked (offset) prefill: S_q queries of sequence b sit at absolute
+ * positions q_pos0[b] + i (i = 0..S_q-1) and attend to a cache of capacity
+ * T_cap whose first kv_lens[b] rows are valid ([MhaMqaGqa] section 7: every
+ * packed row keeps its own causal position; [Ch09] 09.2: absolute positions).
+ * Key j is visible to query i iff j < kv_lens[b] and (mask == NONE or
+ * j <= q_pos0[b] + i).  With q_pos0 = 0, S_q = T_cap = T and kv_lens = T this
+ * is gqa_prefill.  q_pos0 == NULL means kv_lens[b] - S_q (the newest S_q
+ * positions); kv_lens == NULL means T_cap.
+ *
+ *   q (B, h_q, S_q, d_h)  k_cache, v_cache (B, h_kv, T_cap, d_h)  o (B, h_q, S_q, d_h)
+ * Errors: as gqa_prefill.
+ */
+int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,
+                      int B, int h_q, int h_kv, int S_q, int T_cap, int d_h,
+                      int mask, const int32_t* kv_lens, const int32_t* q_pos0,
+                      float scale, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Bytes of device workspace gqa_decode needs for these sizes (any
+ * max_seq_len <= T_cap).  Returns 0 for invalid sizes and for the fp32 path,
+ * which needs none.  `in_dtype` selects the path.
+ */
+size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int T_cap, int d_h, int in_dtype);
+
+/*
+ * Decode: one query per sequence (S_q = 1) attends to its KV cache in place,
+ * every query head a reading cache head g(a) ([EffSeq] 缓存字节; [MhaMqaGqa]
+ * section 7).  The query of sequence b sits at absolute position
+ * p_b = q_pos[b] (q_pos == NULL: seq_lens[b] - 1) and sees keys
+ * j < min(seq_lens[b], p_b + 1, max_seq_len) (clamped to [0, T_cap]).
+ * The history is split across workgroups and the partial softmax states are
+ * merged ([AttnVar] 3.5; [MhaMqaGqa] section 9).
+ *
+ *   q (B, h_q, 1, d_h) in_dtype     k_cache, v_cache (B, h_kv, T_cap, d_h) in_dtype
+ *   seq_lens (B,) int32 = valid cache rows, the current token included
+ *   q_pos (B,) int32 or NULL       o (B, h_q, 1, d_h) out_dtype
+ *   max_seq_len: host bound on the visible length used to size the grid;
+ *     <= 0 means T_cap; must be <= T_cap.
+ *   workspace: device scratch of at least gqa_decode_workspace_bytes(...)
+ *     bytes (may be NULL when that is 0); contents need no initialisation.
+ * Errors: as gqa_prefill, plus max_seq_len > T_cap (INVALID_ARGUMENT) and
+ * GQA_ERR_WORKSPACE_TOO_SMALL.
+ */
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* seq_lens, const int32_t* q_pos, void* o,
+               int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+               float scale, int in_dtype, int out_dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Append one new token's key and value to each sequence's cache: row
+ * write_pos[b] of every cache head of sequence b receives k_new[b, :, 0, :]
+ * and v_new[b, :, 0, :] ([AttnVar] 3.1; [MhaMqaGqa] section 4).  A write_pos
+ * outside [0, T_cap) skips that sequence.  Lengths are the caller's: this
+ * call never changes seq_lens, so appending the same token twice is the
+ * caller's error ([Ch09] 09.4).
+ *
+ *   k_cache, v_cache (B, h_kv, T_cap, d_h) dtype   k_new, v_new (B, h_kv, 1, d_h) dtype
+ *   write_pos (B,) int32
+ * Errors: GQA_ERR_INVALID_ARGUMENT for a size < 1, a NULL or misaligned
+ * pointer, an unknown dtype.
+ */
+int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h,
+                  int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gqa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

@@ -1,0 +1,102 @@
+"""The C-ABI library loads and exports every entry point include/gqa.h declares.
+
+CPU only: calls made here return from host-side validation before any HIP call,
+so no GPU is touched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from grouped_query_attention_prefill_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH), reason="libgqa.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
+              "gqa_kv_append", "gqa_status_string"):
+        assert n in names
+    assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ops.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+@needs_lib
+def test_status_strings():
+    for s in range(5):
+        assert ops.gqa_status_string(s).startswith("GQA_")
+    assert "unknown" in ops.gqa_status_string(99)
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any launch
+
+
+@needs_lib
+@pytest.mark.parametrize("args,expect", [
+    # (B, h_q, h_kv, T, d_h, mask, scale, in, out)
+    ((1, 6, 4, 8, 64, 1, 0.125, 1, 0), ops.GQA_ERR_INVALID_ARGUMENT),    # 6 % 4 != 0
+    ((0, 4, 2, 8, 64, 1, 0.125, 1, 0), ops.GQA_ERR_INVALID_ARGUMENT),    # B < 1
+    ((1, 4, 2, 8, 64, 7, 0.125, 1, 0), ops.GQA_ERR_INVALID_ARGUMENT),    # unknown mask
+    ((1, 4, 2, 8, 64, 1, float("nan"), 1, 0), ops.GQA_ERR_INVALID_ARGUMENT),
+    ((1, 4, 2, 8, 64, 1, -1.0, 1, 0), ops.GQA_ERR_INVALID_ARGUMENT),
+    ((1, 4, 2, 8, 96, 1, 0.1, 1, 0), ops.GQA_ERR_UNSUPPORTED),           # bf16 d_h 96
+    ((1, 4, 2, 8, 300, 1, 0.1, 0, 0), ops.GQA_ERR_UNSUPPORTED),          # fp32 d_h > 256
+    ((1, 4, 2, 8, 64, 1, 0.1, 0, 1), ops.GQA_ERR_UNSUPPORTED),           # fp32 in, bf16 out
+    ((1, 4, 2, 8, 64, 1, 0.1, 5, 0), ops.GQA_ERR_UNSUPPORTED),           # unknown dtype
+])
+def test_prefill_validation(args, expect):
+    lib = ops.load_library()
+    B, h_q, h_kv, T, d_h, mask, scale, i, o = args
+    assert lib.gqa_prefill(FAKE, FAKE, FAKE, FAKE, B, h_q, h_kv, T, d_h, mask, None, scale, i, o, None) == expect
+
+
+@needs_lib
+def test_prefill_rejects_null_and_misaligned():
+    lib = ops.load_library()
+    assert lib.gqa_prefill(None, FAKE, FAKE, FAKE, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_prefill(FAKE + 2, FAKE, FAKE, FAKE, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_prefill(FAKE, FAKE, FAKE, FAKE + 4, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == ops.GQA_ERR_INVALID_ARGUMENT
+
+
+@needs_lib
+def test_decode_validation_and_workspace():
+    lib = ops.load_library()
+    ws = lib.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128, ops.GQA_BF16)
+    assert ws > 0 and ws % 4 == 0
+    assert lib.gqa_decode_workspace_bytes(64, 30, 8, 8192, 128, ops.GQA_BF16) == 0     # invalid sizes
+    assert lib.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128, ops.GQA_F32) == 0      # fp32 path needs none
+    args = (FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 32, 8, 8192, 128, 0, 0.088, ops.GQA_BF16, ops.GQA_F32)
+    # workspace too small
+    assert lib.gqa_decode(*args, FAKE, ws - 1, None) == ops.GQA_ERR_WORKSPACE_TOO_SMALL
+    # max_seq_len above capacity
+    bad = list(args); bad[11] = 8193
+    assert lib.gqa_decode(*bad, FAKE, ws, None) == ops.GQA_ERR_INVALID_ARGUMENT
+    # missing seq_lens
+    bad = list(args); bad[3] = None
+    assert lib.gqa_decode(*bad, FAKE, ws, None) == ops.GQA_ERR_INVALID_ARGUMENT
+
+
+@needs_lib
+def test_kv_append_validation():
+    lib = ops.load_library()
+    assert lib.gqa_kv_append(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 8, 64, 1, None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 64, 9, None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_kv_append(FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 64, 1, None) == ops.GQA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,142 @@
+"""GPU parity of KV-cached decode and kv_append against the float64 oracle."""
+
+import numpy as np
+import pytest
+
+import oracle
+from grouped_query_attention_prefill_amd import inputs, ops
+from tests.gpu_util import check_parity, f64, ints_dev, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(x, dtype, *, q_pos=None, max_seq_len=None, out_dtype=None):
+    import torch
+
+    od = None if out_dtype is None else {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    o = ops.gqa_decode(to_dev(x["q"], dtype), to_dev(x["k_cache"], dtype), to_dev(x["v_cache"], dtype),
+                       ints_dev(x["seq_lens"]), q_pos=None if q_pos is None else ints_dev(q_pos),
+                       max_seq_len=max_seq_len, out_dtype=od)
+    torch.cuda.synchronize()
+    return to_host64(o)
+
+
+def _oracle_decode(x, dtype, q_pos=None):
+    B = x["q"].shape[0]
+    lens = np.asarray(x["seq_lens"])
+    qp = (lens - 1) if q_pos is None else np.asarray(q_pos)
+    out = []
+    for b in range(B):
+        L = int(min(lens[b], qp[b] + 1))
+        out.append(oracle.attention(f64(x["q"][b:b + 1], dtype), f64(x["k_cache"][b:b + 1, :, :L], dtype),
+                                    f64(x["v_cache"][b:b + 1, :, :L], dtype), causal=True,
+                                    q_pos=np.array([[qp[b]]]), kv_len=np.array([L]))[0])
+    return np.stack(out)
+
+
+DECODE_CASES = [
+    # dtype, B, h_q, h_kv, T_cap, d_h, lens
+    ("bf16", 3, 8, 2, 1000, 128, [1000, 517, 1]),
+    ("bf16", 2, 32, 1, 3000, 128, [3000, 2999]),      # MQA, r=32: a full 32-column tile
+    ("bf16", 1, 64, 1, 700, 128, [700]),              # r=64: two head chunks
+    ("bf16", 2, 4, 4, 2100, 64, [2100, 1300]),        # MHA, d_h 64
+    ("bf16", 2, 12, 4, 257, 128, [257, 129]),         # r=3, lengths straddling tiles
+    ("bf16", 4, 32, 8, 9000, 128, [9000, 8192, 4097, 33]),
+    ("f32", 3, 8, 2, 300, 40, [300, 151, 1]),
+    ("f32", 1, 32, 1, 100, 128, [100]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "%s_B%d_hq%d_hkv%d_T%d_d%d" % c[:6])
+def test_decode_parity(case):
+    dt, B, h_q, h_kv, T_cap, d, lens = case
+    print(f"case decode {case[:6]}", flush=True)
+    x = inputs.make_decode(B, h_q, h_kv, d, T_cap, dt, 10000 + T_cap, seq_lens=lens, poison=True)
+    got = _decode(x, dt)
+    check_parity(got, _oracle_decode(x, dt), mode="f32" if dt == "f32" else "bf16", what=str(case[:6]))
+
+
+def test_decode_explicit_positions_and_hint():
+    # q_pos below seq_len - 1 hides the newer rows; max_seq_len sizes the grid
+    x = inputs.make_decode(3, 16, 4, 128, 5000, "bf16", 11000, seq_lens=[5000, 4000, 3000], poison=True)
+    qp = np.array([2500, 3999, 10], np.int32)
+    got = _decode(x, "bf16", q_pos=qp, max_seq_len=5000)
+    check_parity(got, _oracle_decode(x, "bf16", q_pos=qp), mode="bf16", what="q_pos")
+
+
+def test_decode_out_bf16():
+    x = inputs.make_decode(2, 8, 2, 128, 1500, "bf16", 11100, seq_lens=[1500, 700], poison=True)
+    check_parity(_decode(x, "bf16", out_dtype="bf16"), _oracle_decode(x, "bf16"), mode="bf16out", what="bf16 out")
+
+
+def test_decode_zero_length_writes_zeros():
+    x = inputs.make_decode(2, 8, 2, 128, 600, "bf16", 11200, seq_lens=[0, 600])
+    got = _decode(x, "bf16")
+    assert np.all(got[0] == 0.0)
+    xx = {k: (v[1:] if hasattr(v, "shape") and v.shape[:1] == (2,) else v) for k, v in x.items()}
+    check_parity(got[1:], _oracle_decode(xx, "bf16"), mode="bf16", what="len 0")
+
+
+def test_decode_equals_last_prefill_row_bf16():
+    import torch
+
+    B, h_q, h_kv, T, d = 2, 8, 2, 700, 128
+    x = inputs.make_prefill(B, h_q, h_kv, d, T, "bf16", 11300)
+    q, k, v = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    pre = ops.gqa_prefill(q, k, v)
+    dec = ops.gqa_decode(q[:, :, T - 1:].contiguous(), k, v, ints_dev([T, T]))
+    torch.cuda.synchronize()
+    a, b = to_host64(pre)[:, :, T - 1], to_host64(dec)[:, :, 0]
+    assert np.max(np.abs(a - b)) <= 1e-2
+
+
+def test_decode_deterministic():
+    x = inputs.make_decode(2, 32, 8, 128, 4000, "bf16", 11400)
+    assert np.array_equal(_decode(x, "bf16"), _decode(x, "bf16"))
+
+
+# ---------------------------------------------------------------- kv_append
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("bf16", 64), ("f32", 40), ("bf16", 3)])
+def test_kv_append_bit_exact(dt, d):
+    import torch
+
+    B, h_kv, T_cap = 4, 3, 50
+    k = inputs.normal(12000, "k", (B, h_kv, T_cap, d), dt)
+    v = inputs.normal(12000, "v", (B, h_kv, T_cap, d), dt)
+    kn = inputs.normal(12000, "k_new", (B, h_kv, 1, d), dt)
+    vn = inputs.normal(12000, "v_new", (B, h_kv, 1, d), dt)
+    wp = np.array([0, 49, 50, -1], np.int32)            # last two are out of range: skipped
+    kd, vd = to_dev(k, dt), to_dev(v, dt)
+    ops.gqa_kv_append(kd, vd, to_dev(kn, dt), to_dev(vn, dt), ints_dev(wp))
+    torch.cuda.synchronize()
+    view = np.int16 if dt == "bf16" else np.float32
+    gk = kd.cpu().view(torch.int16).numpy() if dt == "bf16" else kd.cpu().numpy()
+    gv = vd.cpu().view(torch.int16).numpy() if dt == "bf16" else vd.cpu().numpy()
+    ek, ev = k.view(view).copy(), v.view(view).copy()
+    for b in range(B):
+        if 0 <= wp[b] < T_cap:
+            ek[b, :, wp[b]] = kn.view(view)[b, :, 0]
+            ev[b, :, wp[b]] = vn.view(view)[b, :, 0]
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+
+
+def test_append_then_decode_ragged_small():
+    import torch
+
+    B, h_q, h_kv, d = 6, 16, 2, 128
+    T_cap = inputs.round_up(2000 + 1, 64)
+    x = inputs.make_append_decode(B, h_q, h_kv, d, T_cap, "bf16", 12100, hist_hi=2000)
+    kd, vd = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+    ops.gqa_kv_append(kd, vd, to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints_dev(x["write_pos"]))
+    o = ops.gqa_decode(to_dev(x["q"], "bf16"), kd, vd, ints_dev(x["seq_lens"]), q_pos=ints_dev(x["q_pos"]),
+                       max_seq_len=int(x["seq_lens"].max()))
+    torch.cuda.synchronize()
+    got = to_host64(o)
+    k = x["k_cache"].copy()
+    v = x["v_cache"].copy()
+    for b in range(B):
+        k[b, :, x["hist"][b]] = x["k_new"][b, :, 0]
+        v[b, :, x["hist"][b]] = x["v_new"][b, :, 0]
+    want = _oracle_decode({"q": x["q"], "k_cache": k, "v_cache": v, "seq_lens": x["seq_lens"]}, "bf16",
+                          q_pos=x["q_pos"])
+    check_parity(got, want, mode="bf16", what="append+decode")

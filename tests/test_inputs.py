@@ -29,13 +29,12 @@ def test_bf16_widening_is_exact():
     assert np.max(np.abs(w - x) / np.abs(x)) <= 2 ** -8
 
 
-def test_determinism_and_draw_order():
+def test_determinism_and_stream_keys():
     a = inputs.make_prefill(1, 4, 2, 8, 5, "bf16", 1950)
     b = inputs.make_prefill(1, 4, 2, 8, 5, "bf16", 1950)
     for key in ("q", "k", "v"):
         assert np.array_equal(a[key], b[key])
-    rng = inputs.rng_for(1950)
-    q0 = rng.standard_normal((4, 5, 8), dtype=np.float32)
+    q0 = inputs.rng_for(1950, inputs.TENSOR_IDS["q"], 0).standard_normal((4, 5, 8), dtype=np.float32)
     assert np.array_equal(inputs.bf16_bits_to_f32(a["q"][0]), inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(q0)))
 
 
