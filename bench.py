@@ -1,0 +1,302 @@
+"""Benchmark of the grouped-query attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-sweep]
+
+Headline step: one causal bf16 prefill of the workload B=1, h_q=32, h_kv=8,
+d_h=128, T=4096 (fp32 output), whose throughput is reported as TFLOP/s of
+algorithmic work (4 h_q d_h FLOPs per visible query/key pair).  The decode
+half of the path is timed in the same run on B=64, h_q=32, h_kv=8, d_h=128,
+T=8192 (HBM GB/s of algorithmic bytes: the visible K/V plus Q and O), and,
+unless --no-sweep, on the MHA / GQA / MQA sweep at T=32000 and the ragged
+append + decode workload.  Inputs are synthetic (seeded N(0,1), bf16) and
+already resident in device memory when each timed region starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
+FLUSH_BYTES = 512 << 20        # larger than the 256 MB Infinity Cache
+METRIC = "GQA decode HBM GB/s (% peak) + causal prefill TFLOP/s (% MFMA peak), 1 GPU"
+
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": ["prefill_bf16.hip", "mfma_common.h"],
+    "decode_bf16_kernel": ["decode_bf16.hip", "mfma_common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "grouped_query_attention_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel, {}).get(workload)
+    if not e or e.get("source_hash") != source_hash(kernel):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_calls(fn, steps: int, warmup: int, flush=None):
+    """Run fn warmup+steps times; HIP events around every timed call on the current stream.
+
+    Returns (wall seconds of the timed region, list of per-call milliseconds).
+    """
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        evs[i][0].record()
+        fn()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in evs]
+
+
+def to_dev(x, dtype):
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def ints(x):
+    import numpy as np
+    import torch
+
+    return torch.as_tensor(np.asarray(x, dtype=np.int32)).cuda()
+
+
+# ---------------------------------------------------------------------------------------- prefill
+def bench_prefill(steps, warmup):
+    import torch
+
+    from grouped_query_attention_prefill_amd import inputs, ops
+
+    w = inputs.WORKLOADS["prefill_causal_bf16_T4096"]
+    log(f"[bench] generating {w.name}")
+    x = inputs.make_workload(w)
+    q, k, v = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    out = torch.empty((w.B, w.h_q, w.T, w.d_h), dtype=torch.float32, device="cuda")
+    # algorithmic work: 4 d_h FLOPs (QK and PV) per visible (query, key) pair per query head
+    flops = 4 * w.B * w.h_q * w.d_h * (w.T * (w.T + 1) // 2)
+    fn = lambda: ops.gqa_prefill(q, k, v, causal=True, out=out)
+    log(f"[bench] timing {w.name}: {warmup} warmup + {steps} steps")
+    wall, per = time_calls(fn, steps, warmup)
+    ms_step = wall * 1e3 / steps
+    kern_ms = sum(per) / len(per)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "workload": w, "x": x, "flops": flops, "ms_per_step": ms_step, "kernel_ms": kern_ms,
+        "value": value, "achieved": achieved,
+    }
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------------------- decode
+def decode_bytes(w, seq_lens, appended: bool):
+    # visible K and V rows (bf16), plus Q (bf16) and O (fp32); the append adds its two rows written
+    kv = sum(2 * w.h_kv * int(L) * w.d_h * 2 for L in seq_lens)
+    qo = w.B * w.h_q * w.d_h * (2 + 4)
+    app = 2 * w.B * w.h_kv * w.d_h * 2 * 2 if appended else 0   # read new rows + write them
+    return kv + qo + app
+
+
+def bench_decode(name, steps, warmup, flush_buf):
+    import numpy as np
+    import torch
+
+    from grouped_query_attention_prefill_amd import inputs, ops
+
+    w = inputs.WORKLOADS[name]
+    log(f"[bench] generating {w.name}")
+    x = inputs.make_workload(w)
+    qd = to_dev(x["q"], "bf16")
+    kd, vd = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+    del x["k_cache"], x["v_cache"]
+    sl, qp = ints(x["seq_lens"]), ints(x["q_pos"])
+    msl = int(x["seq_lens"].max())
+    out = torch.empty((w.B, w.h_q, 1, w.d_h), dtype=torch.float32, device="cuda")
+    ws_bytes = ops.gqa_decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.T, w.d_h, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    appended = w.path == "append_decode"
+    if appended:
+        kn, vn, wp = to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints(x["write_pos"])
+
+        def fn():
+            ops.gqa_kv_append(kd, vd, kn, vn, wp)
+            ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
+    else:
+        fn = lambda: ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
+    flush = lambda: flush_buf.zero_()
+    log(f"[bench] timing {w.name}: {warmup} warmup + {steps} steps (Infinity Cache flushed before each)")
+    wall, per = time_calls(fn, steps, warmup, flush=flush)
+    kern_ms = sum(per) / len(per)
+    nbytes = decode_bytes(w, x["seq_lens"], appended)
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "workload": w.name, "B": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "d_h": w.d_h, "T_cap": w.T,
+        "max_seq_len": msl, "algorithmic_bytes": nbytes, "ms_per_call": round(kern_ms, 5),
+        "value": round(gbs, 1), "unit": "GB/s",
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("decode_bf16_kernel", w.name)},
+        "kernels": ("kv_append + " if appended else "") + "decode split + combine",
+    }
+    del qd, kd, vd, out, ws
+    torch.cuda.empty_cache()
+    return res, x
+
+
+# ---------------------------------------------------------------------------------------- CPU oracle
+def cpu_baseline_prefill(res, budget_s=20.0):
+    import numpy as np
+
+    import oracle
+    from grouped_query_attention_prefill_amd import inputs
+
+    w, x = res["workload"], res["x"]
+    r = w.h_q // w.h_kv
+    cores = len(os.sched_getaffinity(0))
+    log(f"[bench] timing the CPU oracle on heads of {w.name} (budget {budget_s:.0f} s, {cores} cores)")
+    done, flops, t0 = 0, 0, time.perf_counter()
+    for a in range(w.h_q):
+        g = a // r
+        qa = inputs.to_f32(x["q"][:, a:a + 1], "bf16").astype(np.float64)
+        kg = inputs.to_f32(x["k"][:, g:g + 1], "bf16").astype(np.float64)
+        vg = inputs.to_f32(x["v"][:, g:g + 1], "bf16").astype(np.float64)
+        oracle.attention(qa, kg, vg, causal=True)
+        done += 1
+        flops += 4 * w.d_h * w.T * (w.T + 1) // 2
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.h_q} query heads of {w.name} at full T={w.T} (float64, materialized S and P), "
+                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+
+
+def cpu_baseline_decode(x, name, n_seq=2):
+    import numpy as np
+
+    import oracle
+    from grouped_query_attention_prefill_amd import inputs
+
+    w = inputs.WORKLOADS[name]
+    dt, nbytes = 0.0, 0
+    for b in range(n_seq):
+        L = int(x["seq_lens"][b])
+        kb = inputs.normal_row(w.seed, "k", b, (w.h_kv, w.T, w.d_h), "bf16")[None, :, :L]
+        vb = inputs.normal_row(w.seed, "v", b, (w.h_kv, w.T, w.d_h), "bf16")[None, :, :L]
+        qb, kb, vb = (inputs.to_f32(a, "bf16").astype(np.float64) for a in (x["q"][b:b + 1], kb, vb))
+        t1 = time.perf_counter()
+        oracle.attention(qb, kb, vb, causal=True, q_pos=np.array([[x["q_pos"][b]]]), kv_len=np.array([L]))
+        dt += time.perf_counter() - t1
+        nbytes += 2 * w.h_kv * L * w.d_h * 2
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "sample": f"{n_seq} of {w.B} sequences of {name}, {dt:.2f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from grouped_query_attention_prefill_amd import ops
+
+    ops.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
+
+    pre = bench_prefill(steps, warmup)
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    dec, dec_x = bench_decode("decode_bf16_B64_T8192", steps, warmup, flush_buf)
+    sweep = []
+    if not args.no_sweep:
+        for name in ("decode_mha_B8_T32000", "decode_gqa_B8_T32000", "decode_mqa_B8_T32000",
+                     "ragged_append_decode_B32"):
+            r, _ = bench_decode(name, steps, warmup, flush_buf)
+            sweep.append(r)
+    del flush_buf
+    torch.cuda.empty_cache()
+
+    w = pre["workload"]
+    line = {
+        "metric": METRIC,
+        "value": round(pre["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(pre["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to bf16, resident in HBM",
+        "config": {"workload": w.name, "B": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "d_h": w.d_h, "T": w.T,
+                   "causal": True, "out_dtype": "fp32", "algorithmic_flops": pre["flops"]},
+        "roofline": {"bound": "mfma", "achieved": round(pre["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre["achieved"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill_bf16_kernel", w.name),
+                     "kernel_ms": round(pre["kernel_ms"], 5)},
+        "decode": dec,
+        "decode_sweep": sweep,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(pre)
+        dec["cpu_baseline"] = cpu_baseline_decode(dec_x, "decode_bf16_B64_T8192")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

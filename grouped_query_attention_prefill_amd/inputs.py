@@ -90,6 +90,12 @@ def normal(seed: int, tensor: str, shape, dtype: str, rows=None) -> np.ndarray:
     return out
 
 
+def normal_row(seed: int, tensor: str, row: int, shape_tail, dtype: str) -> np.ndarray:
+    """Leading-index slice ``row`` of ``normal(seed, tensor, (B,) + shape_tail, dtype)``, alone."""
+    x = rng_for(seed, TENSOR_IDS[tensor], row).standard_normal(tuple(shape_tail), dtype=np.float32)
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
 def ragged_lengths(seed: int, B: int, lo: int = 1, hi: int = 32768) -> np.ndarray:
     return rng_for(seed, TENSOR_IDS["lengths"]).integers(lo, hi, size=B, endpoint=True).astype(np.int32)
 

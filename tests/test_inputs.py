@@ -56,3 +56,9 @@ def test_named_workloads():
     assert w["ragged_append_decode_B32"].T == 32832
     x = inputs.make_workload(w["tiny_prefill_f32"])
     assert x["q"].dtype == np.float32 and x["q"].shape == (1, 4, 3, 2)
+
+
+def test_normal_row_matches_full_draw():
+    full = inputs.normal(77, "k", (3, 2, 5, 4), "bf16")
+    for b in range(3):
+        assert np.array_equal(inputs.normal_row(77, "k", b, (2, 5, 4), "bf16"), full[b])
