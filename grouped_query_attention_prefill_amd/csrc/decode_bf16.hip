@@ -45,9 +45,9 @@ struct DecodeParams {
 template <int D>
 struct DecodeLds {
   static constexpr int KS = D * 2 + 16;
-  static constexpr int VS = kTile * 2 + 16;
+  static constexpr int VS = D * 2 + 32;
   static constexpr int K_BYTES = kTile * KS;
-  static constexpr int STAGE = K_BYTES + D * VS;
+  static constexpr int STAGE = K_BYTES + kTile * VS;
   // the end-of-slice merge reuses the stage: 4 waves x 32 rows x D floats + (m, l)
   static constexpr int MERGE = 4 * 32 * D * 4 + 4 * 32 * 2 * 4;
   static constexpr int TOTAL = STAGE > MERGE ? STAGE : MERGE;
@@ -119,52 +119,30 @@ decode_bf16_kernel(DecodeParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
-  const uint16_t* kg = p.k + kv_base;
-  const uint16_t* vg = p.v + kv_base;
+  const uint32_t slice_bytes = (uint32_t)hi * D * 2;          // keys >= hi read as zeros
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice_bytes);
 
-  constexpr int K_UNITS = kTile * D / 8 / kThreads;        // 16-byte chunks
-  constexpr int V_UNITS = (kTile / 8) * (D / 2) / kThreads;
-  uint4 kreg[K_UNITS];
-  uint32_t vreg[V_UNITS][8];
-
+  constexpr int UNITS = kTile * D / 8 / kThreads;           // 16-byte chunks per thread per tensor
+  uint4 kreg[UNITS], vreg[UNITS];
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < K_UNITS; ++i) {
+    for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      const int key = k0 + row;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (key < hi) kreg[i] = *reinterpret_cast<const uint4*>(kg + (size_t)key * D + c8 * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int dp = u % (D / 2), ks = u / (D / 2);
-      const int kc = ks >> 1, hs = ks & 1;
-#pragma unroll
-      for (int t2 = 0; t2 < 8; ++t2) {
-        const int key = k0 + chunk_key(kc, hs, t2);
-        vreg[i][t2] = 0u;
-        if (key < hi) vreg[i][t2] = *reinterpret_cast<const uint32_t*>(vg + (size_t)key * D + 2 * dp);
-      }
+      const uint32_t off = (uint32_t)((k0 + row) * D + c8 * 8) * 2;
+      kreg[i] = load16(krs, off);
+      vreg[i] = load16(vrs, off);
     }
   };
   auto store_tile = [&]() {
-    unsigned char* vt_ = lds + L::K_BYTES;
+    unsigned char* vs_ = lds + L::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < K_UNITS; ++i) {
+    for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
       *reinterpret_cast<uint4*>(lds + row * L::KS + c8 * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int dp = u % (D / 2), ks = u / (D / 2);
-      uint4 lo4, hi4;
-      split_pairs(vreg[i], lo4, hi4);
-      *reinterpret_cast<uint4*>(vt_ + (2 * dp) * L::VS + ks * 16) = lo4;
-      *reinterpret_cast<uint4*>(vt_ + (2 * dp + 1) * L::VS + ks * 16) = hi4;
+      *reinterpret_cast<uint4*>(vs_ + row * L::VS + c8 * 16) = vreg[i];
     }
   };
 
@@ -177,15 +155,13 @@ decode_bf16_kernel(DecodeParams p) {
     if (t + 1 < n_tiles) load_tile(k0 + kTile);
     lds_barrier();                 // tile t is in LDS
 
-    const unsigned char* vt_ = lds + L::K_BYTES;
+    const unsigned char* vs_ = lds + L::K_BYTES;
     const int kw = wave * 32;      // this wave's 32-key block of the tile
     f32x16 sacc;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-#pragma unroll
     for (int kd = 0; kd < D / 16; ++kd) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + (kw + col) * L::KS + (kd * 16 + h * 8) * 2);
-      sacc = mfma32(a, qf[kd], sacc);
+      sacc = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc);
     }
     if (k0 + kTile > hi) {
 #pragma unroll
@@ -198,11 +174,17 @@ decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
     mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * p.c);
-    const float mc = m_use * p.c;
-    m_run = m_new;
+    const bool grow = (mx - m_run) * p.c > kLazyRescale;     // false for -inf - (-inf)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2((m_run - mx) * p.c) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m_run = grow ? mx : m_run;
+    }
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * p.c;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -210,11 +192,7 @@ decode_bf16_kernel(DecodeParams p) {
       sacc[e] = pe;
       psum += pe;
     }
-    l_run = alpha * l_run + psum;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    l_run += psum;
     bf16x8 pf[2];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
@@ -222,13 +200,12 @@ decode_bf16_kernel(DecodeParams p) {
       pf[c2] = pack_bf16x8(sacc[e0], sacc[e0 + 1], sacc[e0 + 2], sacc[e0 + 3],
                            sacc[e0 + 4], sacc[e0 + 5], sacc[e0 + 6], sacc[e0 + 7]);
     }
-    // chunks of this wave's block: kc = 2 * wave + c2 in the tile's V^T slot order
+    // chunks of this wave's block: kc = 2 * wave + c2 of the tile
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const int kc = 2 * wave + c2;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt_ + (db * 32 + col) * L::VS + (kc * 16 + h * 8) * 2);
+        const bf16x8 a = load_vt_operand(vs_, L::VS, 2 * wave + c2, db * 32, lane);
         oacc[db] = mfma32(a, pf[c2], oacc[db]);
       }
   }

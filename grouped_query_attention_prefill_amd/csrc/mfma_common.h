@@ -56,26 +56,53 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Interleave two bf16 lanes of 8 dwords: lo -> the low halves, hi -> the high halves.
-// x[t] holds (d, d+1) of key t; the result rows hold 8 keys of one d.
-__device__ __forceinline__ void split_pairs(const uint32_t x[8], uint4& lo, uint4& hi) {
-  lo.x = (x[0] & 0xffffu) | (x[1] << 16);
-  lo.y = (x[2] & 0xffffu) | (x[3] << 16);
-  lo.z = (x[4] & 0xffffu) | (x[5] << 16);
-  lo.w = (x[6] & 0xffffu) | (x[7] << 16);
-  hi.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
-  hi.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
-  hi.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
-  hi.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Buffer resource over [base, base + bytes): loads at or past `bytes` return 0
+// (checked per dword), which zero-fills partial tiles without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// A operand of O^T += V^T P^T for 16 keys (chunk kc of the LDS tile) and 32 values
+// of d starting at d0, read from row-major V in LDS with two transposing reads.
+// ds_read_b64_tr_b16 works in groups of 16 lanes: source lane s = 4j + q supplies
+// 4 consecutive 16-bit values, and output lane i receives, as its value j, element
+// i % 4 of source lane 4j + i / 4.  Pointing source lane (j, q) of group G at row
+// (16 kc + 8u + 4(G / 2) + j), columns d0 + 16(G % 2) + 4q .. +3 hands output lane
+// l the values V[16 kc + 8u + 4(l / 32) + j][d0 + l % 32], j = 0..3: exactly the
+// keys chunk_key() assigns to slots 4u .. 4u + 3 of lane half l / 32.
+__device__ __forceinline__ bf16x8 load_vt_operand(const unsigned char* vrow0, int vs_bytes, int kc, int d0,
+                                                  int lane) {
+  const int G = lane >> 4, s = lane & 15;
+  const int j = s >> 2, q = s & 3;
+  const unsigned char* base = vrow0 + (16 * kc + 4 * (G >> 1) + j) * vs_bytes + (d0 + 16 * (G & 1) + 4 * q) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * vs_bytes));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // Key held by slot t (0..7) of lane half h within 16-key chunk kc of a tile:
 // slots 0..7 of half h are keys {4h..4h+3, 8+4h..8+4h+3}.  This is the key order
 // in which the S^T accumulator rows come out of the matrix core, so P feeds the
-// next product straight from registers; V^T is stored in LDS in the same order.
+// next product straight from registers; load_vt_operand() reads V in that order.
 __device__ __forceinline__ int chunk_key(int kc, int h, int t) {
   return kc * 16 + 8 * (t >> 2) + 4 * h + (t & 3);
 }
+
+// Running maximum is only moved when a tile's maximum exceeds it by more than
+// this many powers of two; until then exp2 arguments stay <= kLazyRescale, the
+// probabilities stay <= 2^kLazyRescale, and the rescale of O and l is skipped.
+// The final o = u / l is unchanged: numerator and denominator carry the same
+// factor ([EffSeq] 在线 softmax: any common base m gives the same ratio).
+constexpr float kLazyRescale = 8.0f;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 

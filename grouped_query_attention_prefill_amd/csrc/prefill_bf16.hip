@@ -10,17 +10,20 @@
 // rows are positions x heads and keep their own causal position).  Per tile,
 // every wave (32 rows) computes
 //     S^T = K Q^T                (matrix core, reduction over d_h)
-//     m'  = max(m, rowmax S)     (lane-local plus one lane-pair exchange)
+//     m'  = max(m, rowmax S)     (lane-local plus one lane-pair exchange; m is only
+//                                 moved when the tile maximum exceeds it by more
+//                                 than 2^kLazyRescale, so most tiles skip the rescale)
 //     P   = exp2(S c - m' c),  c = scale * log2(e)
 //     l   = e^{m - m'} l + rowsum P,   O^T = e^{m - m'} O^T + V^T P^T   (matrix core)
 // and after the last tile writes O = O^T / l.  Keys a row cannot see are
 // removed by selection before the maximum; tiles past the causal frontier
 // are never visited; a row that sees no key is written as zeros.
 //
-// Layouts in LDS (two stages, double-buffered):
-//   K   [64 keys][d_h] row-major, rows padded by 16 bytes (conflict-free reads)
-//   V^T [d_h][64 keys] with keys in chunk_key() order, rows padded by 16 bytes,
-//       built from 4-byte global loads (2 values of d) of 8 keys per thread.
+// Layouts in LDS (two stages, double-buffered), both filled by 16-byte buffer
+// loads that return zeros past the last visible key (no per-load branches):
+//   K [64 keys][d_h] row-major, rows padded by 16 bytes (conflict-free 16-byte reads)
+//   V [64 keys][d_h] row-major, rows padded by 32 bytes (conflict-free transposing
+//     reads, which hand the PV product its V^T operand directly).
 #include "internal.h"
 #include "mfma_common.h"
 
@@ -49,9 +52,9 @@ struct PrefillParams {
 template <int D>
 struct PrefillLds {
   static constexpr int KS = D * 2 + 16;          // K row stride, bytes
-  static constexpr int VS = kTile * 2 + 16;      // V^T row stride, bytes
+  static constexpr int VS = D * 2 + 32;          // V row stride, bytes
   static constexpr int K_BYTES = kTile * KS;
-  static constexpr int STAGE = K_BYTES + D * VS;
+  static constexpr int STAGE = K_BYTES + kTile * VS;
   static constexpr int TOTAL = 2 * STAGE;
 };
 
@@ -117,56 +120,32 @@ prefill_bf16_kernel(PrefillParams p) {
   float l_run = 0.f;         // this lane's share of the normalizer
 
   const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
-  const uint16_t* kg = p.k + kv_base;
-  const uint16_t* vg = p.v + kv_base;
+  const uint32_t slice_bytes = (uint32_t)kv_end * D * 2;     // keys >= kv_end read as zeros
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice_bytes);
 
-  // ---- tile loader: global -> registers -> LDS
-  constexpr int K_UNITS = kTile * D / 8 / kThreads;       // 16-byte K chunks per thread
-  constexpr int V_UNITS = 8 * (D / 2) / kThreads;         // (8-key set, d pair) units per thread
-  uint4 kreg[K_UNITS];
-  uint32_t vreg[V_UNITS][8];
-
+  // ---- tile loader: global -> registers -> LDS, 16 bytes per access
+  constexpr int UNITS = kTile * D / 8 / kThreads;          // 16-byte chunks per thread per tensor
+  uint4 kreg[UNITS], vreg[UNITS];
   auto load_tile = [&](int t) {
-    const int k0 = t * kTile;
 #pragma unroll
-    for (int i = 0; i < K_UNITS; ++i) {
+    for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      const int key = k0 + row;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (key < kv_end) kreg[i] = *reinterpret_cast<const uint4*>(kg + (size_t)key * D + c8 * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int dp = u % (D / 2), ks = u / (D / 2);
-      const int kc = ks >> 1, hs = ks & 1;
-#pragma unroll
-      for (int t2 = 0; t2 < 8; ++t2) {
-        const int key = k0 + chunk_key(kc, hs, t2);
-        vreg[i][t2] = 0u;
-        if (key < kv_end) vreg[i][t2] = *reinterpret_cast<const uint32_t*>(vg + (size_t)key * D + 2 * dp);
-      }
+      const uint32_t off = (uint32_t)((t * kTile + row) * D + c8 * 8) * 2;
+      kreg[i] = load16(krs, off);
+      vreg[i] = load16(vrs, off);
     }
   };
   auto store_tile = [&](int stage) {
     unsigned char* ks_ = lds + stage * L::STAGE;
-    unsigned char* vt_ = ks_ + L::K_BYTES;
+    unsigned char* vs_ = ks_ + L::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < K_UNITS; ++i) {
+    for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
       *reinterpret_cast<uint4*>(ks_ + row * L::KS + c8 * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int dp = u % (D / 2), ks = u / (D / 2);
-      uint4 lo, hi;
-      split_pairs(vreg[i], lo, hi);
-      // slots ks*8 .. ks*8+7 of rows d = 2 dp and 2 dp + 1
-      *reinterpret_cast<uint4*>(vt_ + (2 * dp) * L::VS + ks * 16) = lo;
-      *reinterpret_cast<uint4*>(vt_ + (2 * dp + 1) * L::VS + ks * 16) = hi;
+      *reinterpret_cast<uint4*>(vs_ + row * L::VS + c8 * 16) = vreg[i];
     }
   };
 
@@ -180,7 +159,7 @@ prefill_bf16_kernel(PrefillParams p) {
     lds_barrier();
 
     const unsigned char* ks_ = lds + (t & 1) * L::STAGE;
-    const unsigned char* vt_ = ks_ + L::K_BYTES;
+    const unsigned char* vs_ = ks_ + L::K_BYTES;
     const int k0 = t * kTile;
 
     // S^T for the two 32-key halves of the tile
@@ -188,11 +167,9 @@ prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
-#pragma unroll
       for (int kd = 0; kd < D / 16; ++kd) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks_ + (kb * 32 + col) * L::KS + (kd * 16 + h * 8) * 2);
-        sacc[kb] = mfma32(a, qf[kd], sacc[kb]);
+        sacc[kb] = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
       }
     }
 
@@ -215,11 +192,18 @@ prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // never -inf - (-inf)
-    const float alpha = fast_exp2((m_run - m_use) * p.c);      // 0 while nothing was visible
-    const float mc = m_use * p.c;
-    m_run = m_new;
+    // move the running maximum only when it grew by more than 2^kLazyRescale
+    const bool grow = (mx - m_run) * p.c > kLazyRescale;     // false for -inf - (-inf)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2((m_run - mx) * p.c) : 1.f;   // 0 on the first visible tile
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m_run = grow ? mx : m_run;
+    }
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * p.c;
 
     float psum = 0.f;
 #pragma unroll
@@ -230,26 +214,22 @@ prefill_bf16_kernel(PrefillParams p) {
         sacc[kb][e] = pe;
         psum += pe;
       }
-    l_run = alpha * l_run + psum;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    l_run += psum;
 
     // P^T fragments: chunk kc of the tile = elements 8*(kc&1) .. +7 of half kc>>1
     bf16x8 pf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const f32x16& s = sacc[kc >> 1];
+      const f32x16& sv = sacc[kc >> 1];
       const int e0 = 8 * (kc & 1);
-      pf[kc] = pack_bf16x8(s[e0], s[e0 + 1], s[e0 + 2], s[e0 + 3], s[e0 + 4], s[e0 + 5], s[e0 + 6], s[e0 + 7]);
+      pf[kc] = pack_bf16x8(sv[e0], sv[e0 + 1], sv[e0 + 2], sv[e0 + 3], sv[e0 + 4], sv[e0 + 5], sv[e0 + 6], sv[e0 + 7]);
     }
     // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt_ + (db * 32 + col) * L::VS + (kc * 16 + h * 8) * 2);
+        const bf16x8 a = load_vt_operand(vs_, L::VS, kc, db * 32, lane);
         oacc[db] = mfma32(a, pf[kc], oacc[db]);
       }
 
