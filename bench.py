@@ -188,7 +188,9 @@ def bench_decode(name, steps, warmup, flush_buf):
 
 
 # ---------------------------------------------------------------------------------------- CPU oracle
-def cpu_baseline_prefill(res, budget_s=20.0):
+def cpu_baseline_prefill(res, min_s=10.0, max_s=30.0):
+    """The float64 oracle on the prefill workload: whole query heads at full T, repeated
+    over passes until at least min_s seconds of CPU work (stopping at max_s)."""
     import numpy as np
 
     import oracle
@@ -197,22 +199,25 @@ def cpu_baseline_prefill(res, budget_s=20.0):
     w, x = res["workload"], res["x"]
     r = w.h_q // w.h_kv
     cores = len(os.sched_getaffinity(0))
-    log(f"[bench] timing the CPU oracle on heads of {w.name} (budget {budget_s:.0f} s, {cores} cores)")
-    done, flops, t0 = 0, 0, time.perf_counter()
-    for a in range(w.h_q):
-        g = a // r
-        qa = inputs.to_f32(x["q"][:, a:a + 1], "bf16").astype(np.float64)
-        kg = inputs.to_f32(x["k"][:, g:g + 1], "bf16").astype(np.float64)
-        vg = inputs.to_f32(x["v"][:, g:g + 1], "bf16").astype(np.float64)
-        oracle.attention(qa, kg, vg, causal=True)
-        done += 1
-        flops += 4 * w.d_h * w.T * (w.T + 1) // 2
-        if time.perf_counter() - t0 > budget_s:
+    log(f"[bench] timing the CPU oracle on {w.name} (>= {min_s:.0f} s, {cores} cores)")
+    heads, flops, t0 = 0, 0, time.perf_counter()
+    while True:
+        for a in range(w.h_q):
+            g = a // r
+            qa = inputs.to_f32(x["q"][:, a:a + 1], "bf16").astype(np.float64)
+            kg = inputs.to_f32(x["k"][:, g:g + 1], "bf16").astype(np.float64)
+            vg = inputs.to_f32(x["v"][:, g:g + 1], "bf16").astype(np.float64)
+            oracle.attention(qa, kg, vg, causal=True)
+            heads += 1
+            flops += 4 * w.d_h * w.T * (w.T + 1) // 2
+            if time.perf_counter() - t0 > max_s:
+                break
+        if time.perf_counter() - t0 >= min_s:
             break
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {w.h_q} query heads of {w.name} at full T={w.T} (float64, materialized S and P), "
-                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+            "sample": f"{heads} query-head passes over {w.name} (all {w.h_q} heads per pass, full T={w.T}, "
+                      f"float64, materialized S and P) in {dt:.1f} s", "seconds": round(dt, 2)}
 
 
 def cpu_baseline_decode(x, name, n_seq=2):
@@ -236,6 +241,19 @@ def cpu_baseline_decode(x, name, n_seq=2):
             "kind": "oracle", "sample": f"{n_seq} of {w.B} sequences of {name}, {dt:.2f} s of oracle time"}
 
 
+def bench_copy(steps, warmup):
+    """Plain 1 GiB device copy: the reference kernel that calibrates HBM byte counters."""
+    import torch
+
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    wall, per = time_calls(lambda: b.copy_(a), steps, warmup)
+    ms = sum(per) / len(per)
+    return {"workload": "device_copy_1GiB", "bytes_read": n, "bytes_written": n, "ms_per_call": round(ms, 5),
+            "value": round(2 * n / (ms * 1e-3) / 1e9, 1), "unit": "GB/s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +261,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy"],
+                    help="run one part alone (for profiler runs); prints that part's JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -256,6 +276,20 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     steps, warmup = max(1, args.steps), max(0, args.warmup)
+
+    if args.only == "copy":
+        print(json.dumps(bench_copy(steps, warmup)), flush=True)
+        return
+    if args.only == "prefill":
+        r = bench_prefill(steps, warmup)
+        print(json.dumps({k: v for k, v in r.items() if k not in ("workload", "x")}), flush=True)
+        return
+    if args.only in ("decode", "sweep"):
+        flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        names = ["decode_bf16_B64_T8192"] if args.only == "decode" else [
+            "decode_mha_B8_T32000", "decode_gqa_B8_T32000", "decode_mqa_B8_T32000", "ragged_append_decode_B32"]
+        print(json.dumps([bench_decode(n, steps, warmup, flush_buf)[0] for n in names]), flush=True)
+        return
 
     pre = bench_prefill(steps, warmup)
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")

@@ -2,13 +2,14 @@
 // chunked prefill, head width 64 or 128, fp32 accumulation.
 //
 // Method ([EffSeq] 分块注意力 and 在线 softmax; [AttnVar] 3.5): the score and
-// probability matrices are never written to memory.  A workgroup owns 128
+// probability matrices are never written to memory.  A workgroup owns 256
 // query rows of one (sequence b, K/V head g) and walks the keys in 64-key
 // tiles.  Each K tile and V tile is loaded from HBM once per workgroup into
 // LDS and serves every query head of the group that the workgroup holds
 // ([MhaMqaGqa] section 7: one K/V tile serves all r query rows of its group;
-// rows are positions x heads and keep their own causal position).  Per tile,
-// every wave (32 rows) computes
+// rows are positions x heads and keep their own causal position); its 8 waves
+// take 32 rows each, so one staged tile feeds 256 rows.  Per tile, every wave
+// computes
 //     S^T = K Q^T                (matrix core, reduction over d_h)
 //     m'  = max(m, rowmax S)     (lane-local plus one lane-pair exchange; m is only
 //                                 moved when the tile maximum exceeds it by more
@@ -21,7 +22,8 @@
 //
 // Layouts in LDS (two stages, double-buffered), both filled by 16-byte buffer
 // loads that return zeros past the last visible key (no per-load branches):
-//   K [64 keys][d_h] row-major, rows padded by 16 bytes (conflict-free 16-byte reads)
+//   K [64 keys][d_h] row-major, rows padded by 8 bytes; the K operand is read as two
+//     8-byte halves, conflict-free at this stride
 //   V [64 keys][d_h] row-major, rows padded by 32 bytes (conflict-free transposing
 //     reads, which hand the PV product its V^T operand directly).
 #include "internal.h"
@@ -30,8 +32,8 @@
 namespace gqa {
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kRowsWG = 128;    // query rows per workgroup
+constexpr int kThreads = 512;   // 8 waves, 2 per SIMD
+constexpr int kRowsWG = 256;    // query rows per workgroup (32 per wave)
 constexpr int kTile = 64;       // keys per tile
 
 struct PrefillParams {
@@ -41,7 +43,7 @@ struct PrefillParams {
   void* o;
   const int32_t* kv_lens;
   const int32_t* q_pos0;
-  int h_q, h_kv, r, hp, P;      // hp heads x P positions = 128 rows per workgroup
+  int h_q, h_kv, r, hp, P;      // hp heads x P positions = 256 rows per workgroup
   int S_q, T_cap;
   int causal, from_end;
   int n_qblocks, n_hchunks;
@@ -51,7 +53,7 @@ struct PrefillParams {
 
 template <int D>
 struct PrefillLds {
-  static constexpr int KS = D * 2 + 16;          // K row stride, bytes
+  static constexpr int KS = D * 2 + 8;           // K row stride, bytes (8-byte reads conflict-free)
   static constexpr int VS = D * 2 + 32;          // V row stride, bytes
   static constexpr int K_BYTES = kTile * KS;
   static constexpr int STAGE = K_BYTES + kTile * VS;
@@ -59,7 +61,7 @@ struct PrefillLds {
 };
 
 template <int D, bool OUT_BF16>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 1)
 prefill_bf16_kernel(PrefillParams p) {
   using L = PrefillLds<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -144,7 +146,9 @@ prefill_bf16_kernel(PrefillParams p) {
     for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<uint4*>(ks_ + row * L::KS + c8 * 16) = kreg[i];
+      uint2* kd = reinterpret_cast<uint2*>(ks_ + row * L::KS + c8 * 16);   // rows are 8-byte aligned
+      kd[0] = make_uint2(kreg[i].x, kreg[i].y);
+      kd[1] = make_uint2(kreg[i].z, kreg[i].w);
       *reinterpret_cast<uint4*>(vs_ + row * L::VS + c8 * 16) = vreg[i];
     }
   };
@@ -165,13 +169,15 @@ prefill_bf16_kernel(PrefillParams p) {
     // S^T for the two 32-key halves of the tile
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kd = 0; kd < D / 16; ++kd) {
 #pragma unroll
-      for (int kd = 0; kd < D / 16; ++kd) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks_ + (kb * 32 + col) * L::KS + (kd * 16 + h * 8) * 2);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = lds_read_bf16x8(ks_ + (kb * 32 + col) * L::KS + (kd * 16 + h * 8) * 2);
         sacc[kb] = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
       }
     }
+    // keep four K operand reads in flight ahead of the products that consume them
+    sched_pipeline<D / 8, 2, 1, 4>();
 
     // mask only where some key of the tile may be invisible to some row
     const bool need_mask = (p.causal && k0 + kTile - 1 > min_pos) || (k0 + kTile > len_b);
@@ -226,12 +232,13 @@ prefill_bf16_kernel(PrefillParams p) {
     }
     // O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int db = 0; db < D / 32; ++db) {
         const bf16x8 a = load_vt_operand(vs_, L::VS, kc, db * 32, lane);
         oacc[db] = mfma32(a, pf[kc], oacc[db]);
       }
+    sched_pipeline<4 * D / 32, 2, 1, 4>();
 
     if (t + 1 < n_tiles) store_tile((t + 1) & 1);
   }
