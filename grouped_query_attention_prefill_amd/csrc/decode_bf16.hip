@@ -24,7 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 128;          // keys per workgroup tile (32 per wave)
-constexpr int kTargetWG = 1024;     // workgroups the split heuristic aims for
+constexpr int kTargetWG = 512;      // workgroups the split heuristic aims for (2 resident per CU)
 constexpr int kMinChunk = 256;      // smallest history slice per workgroup
 
 struct DecodeParams {
