@@ -14,8 +14,11 @@
 // and each slice yields a partial state (m, l, u) that the combine kernel
 // merges with the rule of [AttnVar] 3.5:
 //     m' = max_s m_s,   l = sum_s e^{m_s - m'} l_s,   u = sum_s e^{m_s - m'} u_s,   o = u / l.
-// Inside a workgroup the 4 waves take interleaved 32-key blocks of each
-// 128-key tile and merge their states in LDS at the end.
+// Inside a workgroup the 4 waves take interleaved key blocks of each tile and
+// merge their states in LDS at the end.  Groups of up to 16 query heads use
+// 16x16 matrix-core tiles (16 keys per wave per 64-key tile), which halves the
+// accumulator registers so that more workgroups share a CU and keep more HBM
+// requests in flight; larger groups use 32x32 tiles over 128-key tiles.
 #include "internal.h"
 #include "mfma_common.h"
 
@@ -39,6 +42,7 @@ struct DecodeParams {
   int h_q, h_kv, r, hc_count, T_cap, max_len;
   int chunk, n_split, n_split_cap;
   int direct;         // one split: write the normalized output directly
+  int interleave;     // splits take interleaved tiles instead of contiguous slices
   float c;            // scale * log2(e)
 };
 
@@ -276,6 +280,234 @@ decode_bf16_kernel(DecodeParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow groups (r <= 16): 16x16 matrix-core tiles.
+//   S^T (16 keys x 16 heads) = K Q^T   v_mfma_f32_16x16x32_bf16, reduction over d_h
+//     A: lane l holds K[key l%16][d = 32 kd + 8 (l/16) .. +7]   (16 bytes from LDS)
+//     B: lane l holds Q[head l%16][same d]                        (registers)
+//     C: lane l, element i holds S^T[key 4 (l/16) + i][head l%16]
+//   O^T (16 d x 16 heads) += V^T P^T   v_mfma_f32_16x16x16_bf16, reduction over 16 keys
+//     A: lane l holds V[key 4 (l/16) + t][d = 16 dt + l%16], t = 0..3: one transposing
+//        LDS read (16-lane group G reads keys 4G..4G+3 of d 16 dt .. 16 dt + 15)
+//     B: lane l holds P[head l%16][key 4 (l/16) + t]: the S^T accumulator itself
+// A head's 16 keys of a block sit in the four lanes l%16 + 16 {0,1,2,3}, so its
+// maximum and sum take one 16-lane and one 32-lane exchange.
+constexpr int kTile16 = 64;         // keys per workgroup tile (16 per wave)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return pair_max(x);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  return pair_sum(x);
+}
+
+template <int D>
+struct Decode16Lds {
+  static constexpr int KS = D * 2 + 16;
+  static constexpr int VS = D * 2 + 32;
+  static constexpr int K_BYTES = kTile16 * KS;
+  static constexpr int STAGE = K_BYTES + kTile16 * VS;
+  static constexpr int MERGE = 4 * 16 * D * 4 + 4 * 16 * 2 * 4;
+  static constexpr int TOTAL = STAGE > MERGE ? STAGE : MERGE;
+};
+
+template <int D, bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads, 4)
+decode16_bf16_kernel(DecodeParams p) {
+  using L = Decode16Lds<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q16 = lane & 15;      // query head of the group held by this lane
+  const int G = lane >> 4;        // lane group: keys 4G .. 4G+3 of a 16-key block
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+
+  // split s takes tiles s, s + n_split, s + 2 n_split, ... of the history, so the
+  // workgroups of one sequence stream neighbouring memory at the same time
+  const int kv_end = visible_end(p, b);
+  const int n_all = (kv_end + kTile16 - 1) / kTile16;
+  const int n_tiles = n_all > split ? (n_all - split + p.n_split - 1) / p.n_split : 0;
+  const int hi = kv_end;
+  const int n_heads_here = p.r;   // <= 16
+
+  if (n_tiles == 0) {
+    if (p.direct) {
+      for (int e = tid; e < n_heads_here * D; e += kThreads) {
+        const int j = e / D, d = e % D;
+        const size_t oi = (size_t)(b * p.h_q + g * p.r + j) * D + d;
+        if constexpr (OUT_BF16) static_cast<uint16_t*>(p.o)[oi] = 0;
+        else static_cast<float*>(p.o)[oi] = 0.f;
+      }
+    }
+    return;
+  }
+
+  const bool q_valid = q16 < n_heads_here;
+  bf16x8 qf[D / 32];
+  {
+    const uint16_t* qrow = p.q + (size_t)(b * p.h_q + g * p.r + q16) * D;
+#pragma unroll
+    for (int kd = 0; kd < D / 32; ++kd) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (q_valid) x = *reinterpret_cast<const uint4*>(qrow + kd * 32 + G * 8);
+      qf[kd] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
+  const uint32_t slice_bytes = (uint32_t)hi * D * 2;          // keys >= hi read as zeros
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice_bytes);
+
+  constexpr int UNITS = kTile16 * D / 8 / kThreads;
+  uint4 kreg[UNITS], vreg[UNITS];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = tid + kThreads * i;
+      const int row = u / (D / 8), c8 = u % (D / 8);
+      const uint32_t off = (uint32_t)((k0 + row) * D + c8 * 8) * 2;
+      kreg[i] = load16(krs, off);
+      vreg[i] = load16(vrs, off);
+    }
+  };
+  auto store_tile = [&]() {
+    unsigned char* vs_ = lds + L::K_BYTES;
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = tid + kThreads * i;
+      const int row = u / (D / 8), c8 = u % (D / 8);
+      *reinterpret_cast<uint4*>(lds + row * L::KS + c8 * 16) = kreg[i];
+      *reinterpret_cast<uint4*>(vs_ + row * L::VS + c8 * 16) = vreg[i];
+    }
+  };
+
+  const int tstride = p.n_split * kTile16;
+  load_tile(split * kTile16);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = (split + t * p.n_split) * kTile16;
+    lds_barrier();                 // every wave is done reading the previous tile
+    store_tile();
+    if (t + 1 < n_tiles) load_tile(k0 + tstride);
+    lds_barrier();                 // tile t is in LDS
+
+    const unsigned char* vs_ = lds + L::K_BYTES;
+    const int kw = wave * 16;      // this wave's 16 keys of the tile
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kd = 0; kd < D / 32; ++kd) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + (kw + q16) * L::KS + (kd * 32 + G * 8) * 2);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kd], sacc, 0, 0, 0);
+    }
+    if (k0 + kTile16 > hi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kw + 4 * G + i;
+        sacc[i] = key < hi ? sacc[i] : -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    mx = quad_max(mx);
+    const bool grow = (mx - m_run) * p.c > kLazyRescale;     // false for -inf - (-inf)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2((m_run - mx) * p.c) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+      m_run = grow ? mx : m_run;
+    }
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * p.c;
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pe[i] = fast_exp2(fmaf(sacc[i], p.c, -mc));
+      l_run += pe[i];
+    }
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 pb;
+    pb[0] = (__bf16)pe[0]; pb[1] = (__bf16)pe[1]; pb[2] = (__bf16)pe[2]; pb[3] = (__bf16)pe[3];
+    const s16x4 pf = __builtin_bit_cast(s16x4, pb);
+    // V^T operand: source lane (j, q) of group G points at row kw + 4G + j, columns 16 dt + 4q
+    const unsigned char* vsrc = vs_ + (kw + 4 * G + ((lane & 15) >> 2)) * L::VS + 4 * (lane & 3) * 2;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + dt * 32));
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pf, oacc[dt], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the 4 waves' states in LDS
+  lds_barrier();
+  float* mo = reinterpret_cast<float*>(lds);              // [wave][D][16]
+  float* mml = mo + 4 * D * 16;                            // [wave][16][2]
+  const float l_all = quad_sum(l_run);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mo[(wave * D + dt * 16 + 4 * G + i) * 16 + q16] = oacc[dt][i];
+  if (G == 0) {
+    mml[(wave * 16 + q16) * 2 + 0] = (m_run == -INFINITY) ? -INFINITY : m_run * p.c;
+    mml[(wave * 16 + q16) * 2 + 1] = l_all;
+  }
+  lds_barrier();
+
+  // thread -> (head j, d range): 16 heads x D values, D / 16 per thread
+  const int j = tid & 15;
+  const int dgrp = tid >> 4;             // 0..15
+  float mw[4], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) { mw[w] = mml[(w * 16 + j) * 2]; M = fmaxf(M, mw[w]); }
+  float wgt[4], lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wgt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
+    lsum += wgt[w] * mml[(w * 16 + j) * 2 + 1];
+  }
+  if (j < n_heads_here) {
+    const int head = g * p.r + j;
+    const size_t pidx = (size_t)(b * p.h_q + head) * p.n_split_cap + split;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const int d = dgrp * (D / 16) + i;
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += wgt[w] * mo[(w * D + d) * 16 + j];
+      if (p.direct) {
+        const size_t oi = (size_t)(b * p.h_q + head) * D + d;
+        if constexpr (OUT_BF16) {
+          __bf16 x = (__bf16)(acc * inv);
+          static_cast<uint16_t*>(p.o)[oi] = __builtin_bit_cast(uint16_t, x);
+        } else {
+          static_cast<float*>(p.o)[oi] = acc * inv;
+        }
+      } else {
+        p.ws_u[pidx * D + d] = acc;
+      }
+    }
+    if (!p.direct && dgrp == 0) {
+      p.ws_ml[pidx * 2 + 0] = M;
+      p.ws_ml[pidx * 2 + 1] = lsum;
+    }
+  }
+}
+
 // Merge the partial states of one (sequence, query head): [AttnVar] 3.5 applied
 // split after split.  One wave per output row.
 template <int D, bool OUT_BF16>
@@ -285,7 +517,9 @@ decode_combine_kernel(DecodeParams p) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
   const int kv_end = visible_end(p, b);
-  const int n = (kv_end + p.chunk - 1) / p.chunk;
+  // live splits: contiguous slices of `chunk` keys, or (interleaved) one tile each round
+  const int n = p.interleave ? min(p.n_split, (kv_end + kTile16 - 1) / kTile16)
+                             : (kv_end + p.chunk - 1) / p.chunk;
   const size_t base = (size_t)(b * p.h_q + head) * p.n_split_cap;
   constexpr int PER = D / 64;
   float M = -INFINITY, Lsum = 0.f, U[PER];
@@ -318,16 +552,29 @@ decode_combine_kernel(DecodeParams p) {
 
 template <int D, bool OUT_BF16>
 hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
-  constexpr int smem = DecodeLds<D>::TOTAL;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_bf16_kernel<D, OUT_BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr_done = true;
+  if (prm.r <= 16) {
+    constexpr int smem = Decode16Lds<D>::TOTAL;
+    static bool attr16 = false;
+    if (!attr16) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode16_bf16_kernel<D, OUT_BF16>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+      if (e != hipSuccess) return e;
+      attr16 = true;
+    }
+    dim3 grid(prm.n_split, prm.h_kv, B);
+    hipLaunchKernelGGL((decode16_bf16_kernel<D, OUT_BF16>), grid, dim3(kThreads), smem, s, prm);
+  } else {
+    constexpr int smem = DecodeLds<D>::TOTAL;
+    static bool attr32 = false;
+    if (!attr32) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_bf16_kernel<D, OUT_BF16>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+      if (e != hipSuccess) return e;
+      attr32 = true;
+    }
+    dim3 grid(prm.n_split, prm.h_kv * prm.hc_count, B);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, OUT_BF16>), grid, dim3(kThreads), smem, s, prm);
   }
-  dim3 grid(prm.n_split, prm.h_kv * prm.hc_count, B);
-  hipLaunchKernelGGL((decode_bf16_kernel<D, OUT_BF16>), grid, dim3(kThreads), smem, s, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.direct) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(prm.h_q, B), dim3(64), 0, s, prm);
@@ -339,9 +586,11 @@ hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
 DecodePlan plan_decode_bf16(int B, int h_q, int h_kv, int T_cap, int D, int len) {
   DecodePlan pl;
   const int r = h_q / h_kv;
-  pl.head_chunks = (r + 31) / 32;
+  const bool narrow = r <= 16;            // 16x16 tiles, 4 workgroups per CU
+  pl.head_chunks = narrow ? 1 : (r + 31) / 32;
   const long long pairs = (long long)B * h_kv * pl.head_chunks;
-  long long cap = (kTargetWG + pairs - 1) / pairs;
+  const long long target = narrow ? 2 * kTargetWG : kTargetWG;
+  long long cap = (target + pairs - 1) / pairs;
   if (cap < 1) cap = 1;
   const long long max_cap = (T_cap + kMinChunk - 1) / kMinChunk;
   if (cap > max_cap) cap = max_cap < 1 ? 1 : max_cap;
@@ -370,6 +619,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.T_cap = a.T_cap; p.max_len = a.max_len;
   p.chunk = pl.chunk; p.n_split = pl.n_split; p.n_split_cap = pl.n_split_cap;
   p.direct = pl.n_split == 1 ? 1 : 0;
+  p.interleave = p.r <= 16 ? 1 : 0;
   p.c = a.scale * kLog2e;
   const size_t u_bytes = (size_t)a.B * a.h_q * pl.n_split_cap * a.D * sizeof(float);
   p.ws_u = static_cast<float*>(a.workspace);
