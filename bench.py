@@ -167,7 +167,9 @@ def bench_decode(name, steps, warmup, flush_buf):
             ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
     else:
         fn = lambda: ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
-    flush = lambda: flush_buf.zero_()
+    # read (not write) a buffer larger than the Infinity Cache: evicts the inputs
+    # without leaving dirty lines to be written back inside the next timed call
+    flush = lambda: flush_buf.sum()
     log(f"[bench] timing {w.name}: {warmup} warmup + {steps} steps (Infinity Cache flushed before each)")
     wall, per = time_calls(fn, steps, warmup, flush=flush)
     kern_ms = sum(per) / len(per)
@@ -285,14 +287,14 @@ def main():
         print(json.dumps({k: v for k, v in r.items() if k not in ("workload", "x")}), flush=True)
         return
     if args.only in ("decode", "sweep"):
-        flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         names = ["decode_bf16_B64_T8192"] if args.only == "decode" else [
             "decode_mha_B8_T32000", "decode_gqa_B8_T32000", "decode_mqa_B8_T32000", "ragged_append_decode_B32"]
         print(json.dumps([bench_decode(n, steps, warmup, flush_buf)[0] for n in names]), flush=True)
         return
 
     pre = bench_prefill(steps, warmup)
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     dec, dec_x = bench_decode("decode_bf16_B64_T8192", steps, warmup, flush_buf)
     sweep = []
     if not args.no_sweep:

@@ -509,13 +509,17 @@ decode16_bf16_kernel(DecodeParams p) {
 }
 
 // Merge the partial states of one (sequence, query head): [AttnVar] 3.5 applied
-// split after split.  One wave per output row.
+// split after split.  Four waves per output row each fold every fourth split,
+// then the four states are folded in LDS.
 template <int D, bool OUT_BF16>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 decode_combine_kernel(DecodeParams p) {
+  __shared__ float st_u[4][D];
+  __shared__ float st_ml[4][2];
   const int head = blockIdx.x;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int kv_end = visible_end(p, b);
   // live splits: contiguous slices of `chunk` keys, or (interleaved) one tile each round
   const int n = p.interleave ? min(p.n_split, (kv_end + kTile16 - 1) / kTile16)
@@ -525,7 +529,7 @@ decode_combine_kernel(DecodeParams p) {
   float M = -INFINITY, Lsum = 0.f, U[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) U[i] = 0.f;
-  for (int s = 0; s < n; ++s) {
+  for (int s = wave; s < n; s += 4) {
     const float ms = p.ws_ml[(base + s) * 2];
     const float ls = p.ws_ml[(base + s) * 2 + 1];
     if (ms == -INFINITY) continue;
@@ -537,15 +541,32 @@ decode_combine_kernel(DecodeParams p) {
     for (int i = 0; i < PER; ++i) U[i] = a * U[i] + w * p.ws_u[(base + s) * D + lane + 64 * i];
     M = Mn;
   }
-  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) st_u[wave][lane + 64 * i] = U[i];
+  if (lane == 0) { st_ml[wave][0] = M; st_ml[wave][1] = Lsum; }
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, st_ml[w][0]);
+  float wgt[4], Lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wgt[w] = st_ml[w][0] == -INFINITY ? 0.f : fast_exp2(st_ml[w][0] - Mt);
+    Lt += wgt[w] * st_ml[w][1];
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
+    float u = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) u += wgt[w] * st_u[w][lane + 64 * i];
     const size_t oi = (size_t)(b * p.h_q + head) * D + lane + 64 * i;
     if constexpr (OUT_BF16) {
-      __bf16 x = (__bf16)(U[i] * inv);
+      __bf16 x = (__bf16)(u * inv);
       static_cast<uint16_t*>(p.o)[oi] = __builtin_bit_cast(uint16_t, x);
     } else {
-      static_cast<float*>(p.o)[oi] = U[i] * inv;
+      static_cast<float*>(p.o)[oi] = u * inv;
     }
   }
 }
@@ -577,7 +598,7 @@ hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.direct) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(prm.h_q, B), dim3(64), 0, s, prm);
+  hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(prm.h_q, B), dim3(256), 0, s, prm);
   return hipGetLastError();
 }
 
