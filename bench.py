@@ -8,7 +8,7 @@ algorithmic work (4 h_q d_h FLOPs per visible query/key pair).  The decode
 half of the path is timed in the same run on B=64, h_q=32, h_kv=8, d_h=128,
 T=8192 (HBM GB/s of algorithmic bytes: the visible K/V plus Q and O), and,
 unless --no-sweep, on the MHA / GQA / MQA sweep at T=32000 and the ragged
-append + decode workload.  Inputs are synthetic (seeded N(0,1), bf16) and
+append + decode workload, over a contiguous cache and over 64-row pages.  Inputs are synthetic (seeded N(0,1), bf16) and
 already resident in device memory when each timed region starts.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -31,6 +31,10 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
 FLUSH_BYTES = 512 << 20        # larger than the 256 MB Infinity Cache
 METRIC = "GQA decode HBM GB/s (% peak) + causal prefill TFLOP/s (% MFMA peak), 1 GPU"
+
+# decode workloads timed besides the headline ones: (workload, page size or 0 for a contiguous cache)
+SWEEP = [("decode_mha_B8_T32000", 0), ("decode_gqa_B8_T32000", 0), ("decode_mqa_B8_T32000", 0),
+         ("ragged_append_decode_B32", 0), ("ragged_append_decode_B32", 64)]
 
 KERNEL_SOURCES = {
     "prefill_bf16_kernel": ["prefill_bf16.hip", "mfma_common.h"],
@@ -141,7 +145,24 @@ def decode_bytes(w, seq_lens, appended: bool):
     return kv + qo + app
 
 
-def bench_decode(name, steps, warmup, flush_buf):
+def paginate_on_device(cache, page_size, seed):
+    """Scatter a contiguous cache (B, h_kv, T_cap, d) into a page pool in shuffled order.
+
+    Returns (pool (B * T_cap / page_size, h_kv, page_size, d), block_table (B, T_cap / page_size) int32).
+    """
+    import numpy as np
+    import torch
+
+    B, h, T, d = cache.shape
+    mp = T // page_size
+    perm = torch.as_tensor(np.random.default_rng(seed).permutation(B * mp), device=cache.device)
+    pages = cache.view(B, h, mp, page_size, d).permute(0, 2, 1, 3, 4).reshape(B * mp, h, page_size, d)
+    pool = torch.empty_like(pages)
+    pool[perm] = pages
+    return pool, perm.view(B, mp).to(torch.int32).contiguous()
+
+
+def bench_decode(name, steps, warmup, flush_buf, page_size=0):
     import numpy as np
     import torch
 
@@ -153,20 +174,31 @@ def bench_decode(name, steps, warmup, flush_buf):
     qd = to_dev(x["q"], "bf16")
     kd, vd = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
     del x["k_cache"], x["v_cache"]
+    bt = None
+    if page_size:
+        kd, bt = paginate_on_device(kd, page_size, w.seed)
+        vd, _ = paginate_on_device(vd, page_size, w.seed)
+        torch.cuda.empty_cache()
     sl, qp = ints(x["seq_lens"]), ints(x["q_pos"])
     msl = int(x["seq_lens"].max())
     out = torch.empty((w.B, w.h_q, 1, w.d_h), dtype=torch.float32, device="cuda")
     ws_bytes = ops.gqa_decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.T, w.d_h, torch.bfloat16)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     appended = w.path == "append_decode"
+    if page_size:
+        dec = lambda: ops.gqa_decode_paged(qd, kd, vd, bt, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
+    else:
+        dec = lambda: ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
     if appended:
         kn, vn, wp = to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints(x["write_pos"])
+        app = (lambda: ops.gqa_kv_append_paged(kd, vd, kn, vn, bt, wp)) if page_size else \
+            (lambda: ops.gqa_kv_append(kd, vd, kn, vn, wp))
 
         def fn():
-            ops.gqa_kv_append(kd, vd, kn, vn, wp)
-            ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
+            app()
+            dec()
     else:
-        fn = lambda: ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
+        fn = dec
     # read (not write) a buffer larger than the Infinity Cache: evicts the inputs
     # without leaving dirty lines to be written back inside the next timed call
     flush = lambda: flush_buf.sum()
@@ -175,16 +207,19 @@ def bench_decode(name, steps, warmup, flush_buf):
     kern_ms = sum(per) / len(per)
     nbytes = decode_bytes(w, x["seq_lens"], appended)
     gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    wname = w.name + (f"_paged{page_size}" if page_size else "")
     res = {
-        "workload": w.name, "B": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "d_h": w.d_h, "T_cap": w.T,
+        "workload": wname, "B": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "d_h": w.d_h, "T_cap": w.T,
         "max_seq_len": msl, "algorithmic_bytes": nbytes, "ms_per_call": round(kern_ms, 5),
         "value": round(gbs, 1), "unit": "GB/s",
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("decode_bf16_kernel", w.name)},
+                     "traffic": measured_traffic("decode_bf16_kernel", wname)},
         "kernels": ("kv_append + " if appended else "") + "decode split + combine",
     }
-    del qd, kd, vd, out, ws
+    if page_size:
+        res["page_size"] = page_size
+    del qd, kd, vd, out, ws, bt
     torch.cuda.empty_cache()
     return res, x
 
@@ -288,9 +323,8 @@ def main():
         return
     if args.only in ("decode", "sweep"):
         flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-        names = ["decode_bf16_B64_T8192"] if args.only == "decode" else [
-            "decode_mha_B8_T32000", "decode_gqa_B8_T32000", "decode_mqa_B8_T32000", "ragged_append_decode_B32"]
-        print(json.dumps([bench_decode(n, steps, warmup, flush_buf)[0] for n in names]), flush=True)
+        runs = [("decode_bf16_B64_T8192", 0)] if args.only == "decode" else SWEEP
+        print(json.dumps([bench_decode(n, steps, warmup, flush_buf, ps)[0] for n, ps in runs]), flush=True)
         return
 
     pre = bench_prefill(steps, warmup)
@@ -298,9 +332,8 @@ def main():
     dec, dec_x = bench_decode("decode_bf16_B64_T8192", steps, warmup, flush_buf)
     sweep = []
     if not args.no_sweep:
-        for name in ("decode_mha_B8_T32000", "decode_gqa_B8_T32000", "decode_mqa_B8_T32000",
-                     "ragged_append_decode_B32"):
-            r, _ = bench_decode(name, steps, warmup, flush_buf)
+        for name, ps in SWEEP:
+            r, _ = bench_decode(name, steps, warmup, flush_buf, ps)
             sweep.append(r)
     del flush_buf
     torch.cuda.empty_cache()

@@ -144,6 +144,61 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   return hip_status(gqa::launch_decode_bf16(a, pl, s));
 }
 
+int gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                     int B, int h_q, int h_kv, int page_size, int n_pages, int max_pages_per_seq, int d_h,
+                     int max_seq_len, float scale, int in_dtype, int out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || page_size < 1 || n_pages < 1 || max_pages_per_seq < 1 || d_h < 1)
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
+  const long long cap = (long long)page_size * max_pages_per_seq;
+  if (cap > 0x7fffffffLL) return GQA_ERR_INVALID_ARGUMENT;
+  const int T_cap = (int)cap;
+  if (max_seq_len > T_cap) return GQA_ERR_INVALID_ARGUMENT;
+  if (!scale_ok(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (in_dtype != GQA_BF16 || page_size % 64 != 0) return GQA_ERR_UNSUPPORTED;
+  int st = check_types(in_dtype, out_dtype, d_h);
+  if (st != GQA_OK) return st;
+  st = check_ptrs(in_dtype, out_dtype, q, k_pages, v_pages, o);
+  if (st != GQA_OK) return st;
+  if (!block_table || !seq_lens || !aligned(block_table, 4) || !aligned(seq_lens, 4) || (q_pos && !aligned(q_pos, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  const int len = max_seq_len > 0 ? max_seq_len : T_cap;
+  DecodeArgs a;
+  a.q = q; a.k = k_pages; a.v = v_pages; a.seq_lens = seq_lens; a.q_pos = q_pos; a.o = o;
+  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.T_cap = T_cap; a.D = d_h; a.max_len = len;
+  a.scale = scale;
+  a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.block_table = block_table; a.page_size = page_size; a.max_pages = max_pages_per_seq; a.n_pages = n_pages;
+  const gqa::DecodePlan pl = gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, len);
+  if (pl.n_split > 1) {
+    if (workspace_bytes < pl.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned(workspace, 16)) return GQA_ERR_INVALID_ARGUMENT;
+  }
+  return hip_status(gqa::launch_decode_bf16(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                        const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
+                        int page_size, int n_pages, int max_pages_per_seq, int d_h, int dtype, void* stream) {
+  if (B < 1 || h_kv < 1 || page_size < 1 || n_pages < 1 || max_pages_per_seq < 1 || d_h < 1)
+    return GQA_ERR_INVALID_ARGUMENT;
+  if ((long long)page_size * max_pages_per_seq > 0x7fffffffLL) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype)) return GQA_ERR_INVALID_ARGUMENT;
+  const int eb = dtype == GQA_BF16 ? 2 : 4;
+  if ((d_h * eb) % 16 != 0) return GQA_ERR_UNSUPPORTED;
+  if (!k_pages || !v_pages || !k_new || !v_new || !block_table || !write_pos) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(block_table, 4) || !aligned(write_pos, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  return hip_status(gqa::launch_kv_append_paged(k_pages, v_pages, k_new, v_new, block_table, write_pos, B, h_kv,
+                                                page_size, n_pages, max_pages_per_seq, d_h, eb,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                   const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h,
                   int dtype, void* stream) {

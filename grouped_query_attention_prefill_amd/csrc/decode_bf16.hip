@@ -43,6 +43,10 @@ struct DecodeParams {
   int chunk, n_split, n_split_cap;
   int direct;         // one split: write the normalized output directly
   int interleave;     // splits take interleaved tiles instead of contiguous slices
+  // paged cache: pages (n_pages, h_kv, page_size, D); token j of sequence b is row
+  // j % page_size of page block_table[b * max_pages + j / page_size]; null = contiguous
+  const int32_t* block_table;
+  int page_size, max_pages, n_pages;
   float c;            // scale * log2(e)
 };
 
@@ -63,6 +67,31 @@ __device__ __forceinline__ int visible_end(const DecodeParams& p, int b) {
   int e = min(len, pos + 1);
   e = min(e, p.max_len);
   return max(e, 0);
+}
+
+// Rows [k0, k0 + rows) of cache head (b, g), k0 a multiple of 64 (and rows <= 64 in
+// paged mode, so the rows lie in one page).  `valid` counts the rows below hi that
+// are backed by memory; a page index outside [0, n_pages) backs none, so its keys
+// are never read and are treated as invisible.
+struct KvSpan {
+  const uint16_t* k;
+  const uint16_t* v;
+  int valid;
+};
+template <int D>
+__device__ __forceinline__ KvSpan kv_span(const DecodeParams& p, int b, int g, int k0, int rows, int hi) {
+  int valid = max(0, min(rows, hi - k0));
+  size_t off = 0;
+  if (valid > 0) {
+    if (p.block_table) {
+      const int pg = p.block_table[(size_t)b * p.max_pages + k0 / p.page_size];
+      if (pg >= 0 && pg < p.n_pages) off = (((size_t)pg * p.h_kv + g) * p.page_size + k0 % p.page_size) * D;
+      else valid = 0;
+    } else {
+      off = ((size_t)(b * p.h_kv + g) * p.T_cap + k0) * D;
+    }
+  }
+  return KvSpan{p.k + off, p.v + off, valid};
 }
 
 template <int D, bool OUT_BF16>
@@ -122,21 +151,28 @@ decode_bf16_kernel(DecodeParams p) {
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
-  const uint32_t slice_bytes = (uint32_t)hi * D * 2;          // keys >= hi read as zeros
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice_bytes);
-
+  // a 128-key tile is two 64-row halves, each read through its own descriptor whose
+  // range ends at the half's last backed row (reads past it return zeros)
   constexpr int UNITS = kTile * D / 8 / kThreads;           // 16-byte chunks per thread per tensor
   uint4 kreg[UNITS], vreg[UNITS];
+  int lim_next[2], lim_cur[2];
   auto load_tile = [&](int k0) {
+    const KvSpan s0 = kv_span<D>(p, b, g, k0, 64, hi);
+    const KvSpan s1 = kv_span<D>(p, b, g, k0 + 64, 64, hi);
+    const __amdgpu_buffer_rsrc_t kr0 = make_rsrc(s0.k, (uint32_t)s0.valid * D * 2);
+    const __amdgpu_buffer_rsrc_t vr0 = make_rsrc(s0.v, (uint32_t)s0.valid * D * 2);
+    const __amdgpu_buffer_rsrc_t kr1 = make_rsrc(s1.k, (uint32_t)s1.valid * D * 2);
+    const __amdgpu_buffer_rsrc_t vr1 = make_rsrc(s1.v, (uint32_t)s1.valid * D * 2);
+    lim_next[0] = k0 + s0.valid;
+    lim_next[1] = k0 + 64 + s1.valid;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      const uint32_t off = (uint32_t)((k0 + row) * D + c8 * 8) * 2;
-      kreg[i] = load16(krs, off);
-      vreg[i] = load16(vrs, off);
+      const bool second = i >= UNITS / 2;                     // rows 64..127 (uniform per i)
+      const uint32_t off = (uint32_t)((row - (second ? 64 : 0)) * D + c8 * 8) * 2;
+      kreg[i] = load16(second ? kr1 : kr0, off);
+      vreg[i] = load16(second ? vr1 : vr0, off);
     }
   };
   auto store_tile = [&]() {
@@ -156,22 +192,25 @@ decode_bf16_kernel(DecodeParams p) {
     const int k0 = lo + t * kTile;
     lds_barrier();                 // every wave is done reading the previous tile
     store_tile();
+    lim_cur[0] = lim_next[0];
+    lim_cur[1] = lim_next[1];
     if (t + 1 < n_tiles) load_tile(k0 + kTile);
     lds_barrier();                 // tile t is in LDS
 
     const unsigned char* vs_ = lds + L::K_BYTES;
     const int kw = wave * 32;      // this wave's 32-key block of the tile
+    const int lim = lim_cur[wave >> 1];   // keys at or past lim are invisible
     f32x16 sacc;
 #pragma unroll
     for (int kd = 0; kd < D / 16; ++kd) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + (kw + col) * L::KS + (kd * 16 + h * 8) * 2);
       sacc = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc);
     }
-    if (k0 + kTile > hi) {
+    if (k0 + kw + 32 > lim) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + kw + 8 * (e >> 2) + 4 * h + (e & 3);
-        sacc[e] = key < hi ? sacc[e] : -INFINITY;
+        sacc[e] = key < lim ? sacc[e] : -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -370,19 +409,21 @@ decode16_bf16_kernel(DecodeParams p) {
   for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
-  const uint32_t slice_bytes = (uint32_t)hi * D * 2;          // keys >= hi read as zeros
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice_bytes);
-
+  // each 64-key tile is read through its own descriptor whose range ends at the
+  // tile's last backed row (reads past it return zeros)
   constexpr int UNITS = kTile16 * D / 8 / kThreads;
   uint4 kreg[UNITS], vreg[UNITS];
+  int lim_next = 0, lim_cur = 0;
   auto load_tile = [&](int k0) {
+    const KvSpan sp = kv_span<D>(p, b, g, k0, kTile16, hi);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(sp.k, (uint32_t)sp.valid * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(sp.v, (uint32_t)sp.valid * D * 2);
+    lim_next = k0 + sp.valid;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      const uint32_t off = (uint32_t)((k0 + row) * D + c8 * 8) * 2;
+      const uint32_t off = (uint32_t)(row * D + c8 * 8) * 2;
       kreg[i] = load16(krs, off);
       vreg[i] = load16(vrs, off);
     }
@@ -404,6 +445,7 @@ decode16_bf16_kernel(DecodeParams p) {
     const int k0 = (split + t * p.n_split) * kTile16;
     lds_barrier();                 // every wave is done reading the previous tile
     store_tile();
+    lim_cur = lim_next;            // keys at or past lim_cur are invisible
     if (t + 1 < n_tiles) load_tile(k0 + tstride);
     lds_barrier();                 // tile t is in LDS
 
@@ -415,11 +457,11 @@ decode16_bf16_kernel(DecodeParams p) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + (kw + q16) * L::KS + (kd * 32 + G * 8) * 2);
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kd], sacc, 0, 0, 0);
     }
-    if (k0 + kTile16 > hi) {
+    if (k0 + kw + 16 > lim_cur) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + kw + 4 * G + i;
-        sacc[i] = key < hi ? sacc[i] : -INFINITY;
+        sacc[i] = key < lim_cur ? sacc[i] : -INFINITY;
       }
     }
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
@@ -641,6 +683,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.chunk = pl.chunk; p.n_split = pl.n_split; p.n_split_cap = pl.n_split_cap;
   p.direct = pl.n_split == 1 ? 1 : 0;
   p.interleave = p.r <= 16 ? 1 : 0;
+  p.block_table = a.block_table;
+  p.page_size = a.page_size; p.max_pages = a.max_pages; p.n_pages = a.n_pages;
   p.c = a.scale * kLog2e;
   const size_t u_bytes = (size_t)a.B * a.h_q * pl.n_split_cap * a.D * sizeof(float);
   p.ws_u = static_cast<float*>(a.workspace);

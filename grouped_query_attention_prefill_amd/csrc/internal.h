@@ -37,6 +37,10 @@ struct DecodeArgs {
   int out_bf16;
   void* workspace;
   size_t workspace_bytes;
+  // paged cache (block_table non-null): k, v point at page pools (n_pages, h_kv,
+  // page_size, D); T_cap = max_pages * page_size
+  const int32_t* block_table = nullptr;
+  int page_size = 0, max_pages = 0, n_pages = 0;
 };
 
 struct DecodePlan {
@@ -57,5 +61,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStrea
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* write_pos, int B, int h_kv, int T_cap, int D,
                             int elem_bytes, hipStream_t s);
+hipError_t launch_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                                  const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
+                                  int page_size, int n_pages, int max_pages, int D, int elem_bytes,
+                                  hipStream_t s);
 
 }  // namespace gqa

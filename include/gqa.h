@@ -154,6 +154,35 @@ int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
                   const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h,
                   int dtype, void* stream);
 
+/*
+ * Paged KV cache (the deployment form the pages list next to the contiguous
+ * cache: [AttnVar] 3.6 names paging fragments, [MhaMqaGqa] §8 page metadata).
+ * Page pools k_pages, v_pages are (n_pages, h_kv, page_size, d_h); token j of
+ * sequence b is row j % page_size of page block_table[b][j / page_size], with
+ * block_table (B, max_pages_per_seq) int32.  The capacity of a sequence is
+ * T_cap = max_pages_per_seq * page_size; everything else is gqa_decode's
+ * contract (positions, lengths, max_seq_len, workspace: size it with
+ * gqa_decode_workspace_bytes(B, h_q, h_kv, T_cap, d_h, in_dtype)).  A page index
+ * outside [0, n_pages) backs no key: its keys are not read and count as
+ * invisible.  Supported: in_dtype GQA_BF16, d_h in {64, 128}, page_size a
+ * multiple of 64; otherwise GQA_ERR_UNSUPPORTED.
+ */
+int gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                     int B, int h_q, int h_kv, int page_size, int n_pages, int max_pages_per_seq, int d_h,
+                     int max_seq_len, float scale, int in_dtype, int out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kv_append into a paged cache: token position write_pos[b] goes to row
+ * write_pos[b] % page_size of page block_table[b][write_pos[b] / page_size].
+ * A position outside [0, T_cap) or an invalid page index skips the sequence.
+ * Rows must be a multiple of 16 bytes (d_h * element size); else UNSUPPORTED.
+ */
+int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                        const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
+                        int page_size, int n_pages, int max_pages_per_seq, int d_h, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* gqa_status_string(int status);
 

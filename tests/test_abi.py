@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
-              "gqa_kv_append", "gqa_status_string"):
+              "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -100,3 +100,26 @@ def test_kv_append_validation():
     assert lib.gqa_kv_append(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 8, 64, 1, None) == ops.GQA_ERR_INVALID_ARGUMENT
     assert lib.gqa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 64, 9, None) == ops.GQA_ERR_INVALID_ARGUMENT
     assert lib.gqa_kv_append(FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 64, 1, None) == ops.GQA_ERR_INVALID_ARGUMENT
+
+
+@needs_lib
+def test_paged_validation():
+    lib = ops.load_library()
+    # (q, kp, vp, bt, sl, qp, o, B, h_q, h_kv, page, n_pages, max_pages, d_h, msl, scale, in, out, ws, wsb, stream)
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 8, 2, 64, 10, 500, 128, 0, 0.088, ops.GQA_BF16, ops.GQA_F32,
+            FAKE, 1 << 30, None]
+    def call(**kw):
+        a = list(base)
+        names = ["q", "kp", "vp", "bt", "sl", "qp", "o", "B", "h_q", "h_kv", "page", "n_pages", "max_pages", "d_h",
+                 "msl", "scale", "in", "out", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.gqa_decode_paged(*a)
+    assert call(page=48) == ops.GQA_ERR_UNSUPPORTED          # page size not a multiple of 64
+    assert call(**{"in": ops.GQA_F32}) == ops.GQA_ERR_UNSUPPORTED
+    assert call(bt=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(msl=500 * 64 + 1) == ops.GQA_ERR_INVALID_ARGUMENT  # above max_pages x page_size
+    assert call(h_q=7) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(wsb=0) == ops.GQA_ERR_WORKSPACE_TOO_SMALL   # 32000 keys per sequence need splits
+    assert lib.gqa_kv_append_paged(FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 2, 64, 10, 4, 128, 1, None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_kv_append_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 10, 4, 3, 1, None) == ops.GQA_ERR_UNSUPPORTED

@@ -1,0 +1,213 @@
+"""GPU parity of decode and kv_append over a paged KV cache.
+
+The page pool is built from a contiguous cache by scattering its pages to
+shuffled pool slots (unused slots and rows hold NaN); the oracle runs on the
+contiguous keys and values a sequence can see, so a wrong page lookup, a wrong
+in-page row or a read of a page the sequence does not own shows up as a
+mismatch or a non-finite output.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from grouped_query_attention_prefill_amd import inputs, ops
+from tests.gpu_util import check_parity, f64, ints_dev, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+def _paginate(cache, page_size, seed, spare=3):
+    """cache (B, h_kv, T_cap, d) with T_cap % page_size == 0 -> pool, block_table."""
+    B, h, T, d = cache.shape
+    assert T % page_size == 0
+    mp = T // page_size
+    n_pages = B * mp + spare
+    perm = np.random.default_rng(seed).permutation(n_pages)[:B * mp].reshape(B, mp)
+    pool = np.full((n_pages, h, page_size, d), NAN_BF16, dtype=cache.dtype)
+    for b in range(B):
+        for p in range(mp):
+            pool[perm[b, p]] = cache[b, :, p * page_size:(p + 1) * page_size]
+    return pool, perm.astype(np.int32)
+
+
+def _decode_paged(q, kp, vp, bt, lens, *, q_pos=None, max_seq_len=None, out_dtype=None):
+    import torch
+
+    od = None if out_dtype is None else {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    o = ops.gqa_decode_paged(to_dev(q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"), ints_dev(bt),
+                             ints_dev(lens), q_pos=None if q_pos is None else ints_dev(q_pos),
+                             max_seq_len=max_seq_len, out_dtype=od)
+    torch.cuda.synchronize()
+    return to_host64(o)
+
+
+def _oracle_rows(x, b, keep):
+    """Oracle output of sequence b over the cache rows listed in `keep` (ascending)."""
+    n = len(keep)
+    return oracle.attention(f64(x["q"][b:b + 1], "bf16"), f64(x["k_cache"][b:b + 1, :, keep], "bf16"),
+                            f64(x["v_cache"][b:b + 1, :, keep], "bf16"), causal=True,
+                            q_pos=np.array([[n - 1]]), kv_len=np.array([n]))[0]
+
+
+PAGED_CASES = [
+    # B, h_q, h_kv, d_h, page_size, max_pages, lens
+    (3, 8, 2, 128, 64, 16, [1000, 517, 1]),          # r=4: 16x16 kernel, interleaved splits
+    (2, 32, 1, 128, 128, 24, [3000, 2999]),          # MQA r=32: 32x32 kernel
+    (1, 64, 1, 128, 256, 3, [700]),                  # r=64: two head chunks
+    (2, 4, 4, 64, 64, 33, [2100, 1300]),             # MHA, d_h 64
+    (2, 12, 4, 128, 192, 2, [257, 129]),             # r=3, page size 3 x 64
+    (4, 32, 8, 128, 64, 141, [9000, 8192, 4097, 33]),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: "B%d_hq%d_hkv%d_d%d_page%d" % c[:5])
+def test_decode_paged_parity(case):
+    B, h_q, h_kv, d, ps, mp, lens = case
+    print(f"case paged {case[:6]}", flush=True)
+    x = inputs.make_decode(B, h_q, h_kv, d, ps * mp, "bf16", 20000 + ps * mp, seq_lens=lens, poison=True)
+    kp, bt = _paginate(x["k_cache"], ps, 1 + B)
+    vp, _ = _paginate(x["v_cache"], ps, 1 + B)
+    got = _decode_paged(x["q"], kp, vp, bt, x["seq_lens"])
+    want = np.stack([_oracle_rows(x, b, np.arange(lens[b])) for b in range(B)])
+    check_parity(got, want, mode="bf16", what=str(case[:6]))
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(8, 2), (64, 2)], ids=["narrow", "wide"])
+def test_decode_paged_equals_contiguous(h_q, h_kv):
+    # the same split plan over the same bytes: results agree bit for bit
+    import torch
+
+    B, d, ps, mp = 3, 128, 64, 40
+    lens = [2560, 1999, 65]
+    x = inputs.make_decode(B, h_q, h_kv, d, ps * mp, "bf16", 20100, seq_lens=lens, poison=True)
+    kp, bt = _paginate(x["k_cache"], ps, 7)
+    vp, _ = _paginate(x["v_cache"], ps, 7)
+    got = _decode_paged(x["q"], kp, vp, bt, x["seq_lens"])
+    o = ops.gqa_decode(to_dev(x["q"], "bf16"), to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16"),
+                       ints_dev(x["seq_lens"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(got, to_host64(o))
+
+
+@pytest.mark.parametrize("h_q,h_kv,ps", [(8, 2, 64), (32, 1, 128), (64, 2, 64)], ids=["narrow", "wide", "wide2"])
+def test_decode_paged_invalid_pages_are_invisible(h_q, h_kv, ps):
+    B, d, mp = 3, 128, 12
+    lens = [ps * mp, ps * 5 + 17, ps * 2]
+    x = inputs.make_decode(B, h_q, h_kv, d, ps * mp, "bf16", 20200 + ps, seq_lens=lens, poison=True)
+    kp, bt = _paginate(x["k_cache"], ps, 11)
+    vp, _ = _paginate(x["v_cache"], ps, 11)
+    n_pages = kp.shape[0]
+    bt[0, 3] = -1              # a hole in the middle of sequence 0
+    bt[0, 7] = n_pages + 5     # and an index past the pool
+    bt[1, 5] = -7              # the partial last page of sequence 1
+    bt[2, :] = -1              # sequence 2 has no page at all: zeros
+    got = _decode_paged(x["q"], kp, vp, bt, x["seq_lens"])
+    keep0 = [j for j in range(lens[0]) if j // ps not in (3, 7)]
+    keep1 = [j for j in range(lens[1]) if j // ps != 5]
+    check_parity(got[0], _oracle_rows(x, 0, np.array(keep0)), mode="bf16", what="holes")
+    check_parity(got[1], _oracle_rows(x, 1, np.array(keep1)), mode="bf16", what="partial page")
+    assert np.all(got[2] == 0.0)
+
+
+def test_decode_paged_positions_hint_and_bf16_out():
+    B, h_q, h_kv, d, ps, mp = 3, 16, 4, 128, 128, 40
+    x = inputs.make_decode(B, h_q, h_kv, d, ps * mp, "bf16", 20300, seq_lens=[5000, 4000, 3000], poison=True)
+    kp, bt = _paginate(x["k_cache"], ps, 13)
+    vp, _ = _paginate(x["v_cache"], ps, 13)
+    qp = np.array([2500, 3999, 10], np.int32)
+    got = _decode_paged(x["q"], kp, vp, bt, x["seq_lens"], q_pos=qp, max_seq_len=5000, out_dtype="bf16")
+    want = np.stack([_oracle_rows(x, b, np.arange(min(x["seq_lens"][b], qp[b] + 1))) for b in range(B)])
+    check_parity(got, want, mode="bf16out", what="paged q_pos")
+
+
+@pytest.mark.parametrize("d", [128, 64, 8])
+def test_kv_append_paged_bit_exact(d):
+    import torch
+
+    B, h_kv, ps, mp = 5, 3, 64, 4
+    k = inputs.normal(21000, "k", (B, h_kv, ps * mp, d), "bf16")
+    v = inputs.normal(21000, "v", (B, h_kv, ps * mp, d), "bf16")
+    kn = inputs.normal(21000, "k_new", (B, h_kv, 1, d), "bf16")
+    vn = inputs.normal(21000, "v_new", (B, h_kv, 1, d), "bf16")
+    kp, bt = _paginate(k, ps, 17)
+    vp, _ = _paginate(v, ps, 17)
+    bt[3, 2] = -1                                        # sequence 3 writes into a missing page: skipped
+    wp = np.array([0, 255, 256, 130, -1], np.int32)      # 256 and -1 are out of range: skipped
+    kd, vd = to_dev(kp, "bf16"), to_dev(vp, "bf16")
+    ops.gqa_kv_append_paged(kd, vd, to_dev(kn, "bf16"), to_dev(vn, "bf16"), ints_dev(bt), ints_dev(wp))
+    torch.cuda.synchronize()
+    ek, ev = kp.copy(), vp.copy()
+    for b in range(B):
+        if 0 <= wp[b] < ps * mp and 0 <= bt[b, wp[b] // ps] < kp.shape[0]:
+            ek[bt[b, wp[b] // ps], :, wp[b] % ps] = kn[b, :, 0]
+            ev[bt[b, wp[b] // ps], :, wp[b] % ps] = vn[b, :, 0]
+    assert np.array_equal(kd.cpu().view(torch.int16).numpy(), ek.view(np.int16))
+    assert np.array_equal(vd.cpu().view(torch.int16).numpy(), ev.view(np.int16))
+
+
+def test_append_then_decode_paged_ragged():
+    import torch
+
+    B, h_q, h_kv, d, ps = 6, 16, 2, 128, 64
+    T_cap = inputs.round_up(2000 + 1, ps)
+    x = inputs.make_append_decode(B, h_q, h_kv, d, T_cap, "bf16", 21100, hist_hi=2000)
+    kp, bt = _paginate(x["k_cache"], ps, 19)
+    vp, _ = _paginate(x["v_cache"], ps, 19)
+    kd, vd, btd = to_dev(kp, "bf16"), to_dev(vp, "bf16"), ints_dev(bt)
+    ops.gqa_kv_append_paged(kd, vd, to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), btd,
+                            ints_dev(x["write_pos"]))
+    o = ops.gqa_decode_paged(to_dev(x["q"], "bf16"), kd, vd, btd, ints_dev(x["seq_lens"]),
+                             q_pos=ints_dev(x["q_pos"]), max_seq_len=int(x["seq_lens"].max()))
+    torch.cuda.synchronize()
+    got = to_host64(o)
+    k, v = x["k_cache"].copy(), x["v_cache"].copy()
+    for b in range(B):
+        k[b, :, x["hist"][b]] = x["k_new"][b, :, 0]
+        v[b, :, x["hist"][b]] = x["v_new"][b, :, 0]
+    xx = {"q": x["q"], "k_cache": k, "v_cache": v}
+    want = np.stack([_oracle_rows(xx, b, np.arange(x["seq_lens"][b])) for b in range(B)])
+    check_parity(got, want, mode="bf16", what="paged append+decode")
+
+
+def test_ragged_append_decode_B32_paged_fullsize():
+    """The ragged workload at full size with 64-row pages scattered over a pool."""
+    import torch
+
+    w = inputs.WORKLOADS["ragged_append_decode_B32"]
+    print(f"case {w.name} paged", flush=True)
+    x = inputs.make_workload(w)
+    ps = 64
+    mp = w.T // ps
+    kd, vd = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+    perm = torch.as_tensor(np.random.default_rng(23).permutation(w.B * mp), device=kd.device)
+
+    def pool_of(c):
+        pages = c.view(w.B, w.h_kv, mp, ps, w.d_h).permute(0, 2, 1, 3, 4).reshape(w.B * mp, w.h_kv, ps, w.d_h)
+        pool = torch.empty_like(pages)
+        pool[perm] = pages
+        return pool
+
+    kp, vp = pool_of(kd), pool_of(vd)
+    btd = perm.view(w.B, mp).to(torch.int32).contiguous()
+    kn, vn, wp = to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints_dev(x["write_pos"])
+    lens, qp, msl = ints_dev(x["seq_lens"]), ints_dev(x["q_pos"]), int(x["seq_lens"].max())
+    ops.gqa_kv_append_paged(kp, vp, kn, vn, btd, wp)
+    got_p = ops.gqa_decode_paged(to_dev(x["q"], "bf16"), kp, vp, btd, lens, q_pos=qp, max_seq_len=msl)
+    ops.gqa_kv_append(kd, vd, kn, vn, wp)
+    got_c = ops.gqa_decode(to_dev(x["q"], "bf16"), kd, vd, lens, q_pos=qp, max_seq_len=msl)
+    torch.cuda.synchronize()
+    got = to_host64(got_p)
+    assert np.array_equal(got, to_host64(got_c))
+    hist = x["hist"]
+    for b in sorted({int(np.argmin(hist)), int(np.argmax(hist)), 9}):
+        L = int(x["seq_lens"][b])
+        k = x["k_cache"][b:b + 1, :, :L].copy()
+        v = x["v_cache"][b:b + 1, :, :L].copy()
+        k[0, :, hist[b]] = x["k_new"][b, :, 0]
+        v[0, :, hist[b]] = x["v_new"][b, :, 0]
+        want = oracle.attention(f64(x["q"][b:b + 1], "bf16"), f64(k, "bf16"), f64(v, "bf16"), causal=True,
+                                q_pos=np.array([[hist[b]]]), kv_len=np.array([L]))
+        check_parity(got[b:b + 1], want, mode="bf16", what=f"paged ragged b={b}")
