@@ -59,14 +59,6 @@ __device__ __forceinline__ void lds_barrier() {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 16 bytes from LDS as two 8-byte reads: on gfx950 a wave of 8-byte LDS reads
-// moves more bytes per clock than a wave of 16-byte reads.
-__device__ __forceinline__ bf16x8 lds_read_bf16x8(const unsigned char* p) {
-  const uint2 lo = *reinterpret_cast<const uint2*>(p);
-  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
-  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
 // Buffer resource over [base, base + bytes): loads at or past `bytes` return 0
 // (checked per dword), which zero-fills partial tiles without branches.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -111,22 +103,6 @@ __device__ __forceinline__ int chunk_key(int kc, int h, int t) {
 // The final o = u / l is unchanged: numerator and denominator carry the same
 // factor ([EffSeq] 在线 softmax: any common base m gives the same ratio).
 constexpr float kLazyRescale = 8.0f;
-
-// Instruction-scheduling shape for a block of N operand groups, each fed by R
-// LDS reads and consumed by M matrix products: the reads of the first AHEAD
-// groups are requested first, then every group's products are followed by the
-// reads of the group AHEAD places later, so LDS latency hides behind the
-// matrix core instead of stalling each product.
-template <int N, int R, int M, int AHEAD>
-__device__ __forceinline__ void sched_pipeline() {
-  __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);      // DS reads
-#pragma unroll
-  for (int i = 0; i < N - AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);            // this group's products
-    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);            // a later group's reads
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, M * AHEAD, 0);
-}
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 

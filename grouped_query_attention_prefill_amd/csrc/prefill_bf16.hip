@@ -8,7 +8,7 @@
 // LDS and serves every query head of the group that the workgroup holds
 // ([MhaMqaGqa] section 7: one K/V tile serves all r query rows of its group;
 // rows are positions x heads and keep their own causal position); its 8 waves
-// take 32 rows each, so one staged tile feeds 256 rows.  Per tile, every wave
+// take 32 rows each, so one staged tile feeds 256 rows.  Per tile t, every wave
 // computes
 //     S^T = K Q^T                (matrix core, reduction over d_h)
 //     m'  = max(m, rowmax S)     (lane-local plus one lane-pair exchange; m is only
@@ -20,19 +20,33 @@
 // removed by selection before the maximum; tiles past the causal frontier
 // are never visited; a row that sees no key is written as zeros.
 //
-// Layouts in LDS (two stages, double-buffered), both filled by 16-byte buffer
-// loads that return zeros past the last visible key (no per-load branches):
-//   K [64 keys][d_h] row-major, rows padded by 8 bytes; the K operand is read as two
-//     8-byte halves, conflict-free at this stride
+// Schedule: the work of a tile is split into a matrix phase (O^T += V^T P^T for
+// the previous tile, then S^T = K Q^T for this one) and a vector phase (mask,
+// maximum, exponentials, row sums, P packed to bf16).  The 8 waves form two
+// groups of four, one wave of each on every SIMD, and the second group runs one
+// phase behind the first: while one wave of a SIMD keeps the matrix core busy,
+// the other does its exponentials, and a workgroup barrier between phases keeps
+// the two groups in step.  The groups also split the staging: the leading group
+// streams K tiles and the trailing group V tiles, each through registers into
+// a double-buffered LDS stage, written in the middle of the group's matrix phase
+// (global loads are requested two phases before their data is written).
+//
+// Layouts in LDS, both filled by 16-byte buffer loads that return zeros past the
+// last visible key (no per-load branches):
+//   K [64 keys][d_h] row-major, rows padded by 16 bytes: 16-byte operand reads
+//     are conflict-free at this stride
 //   V [64 keys][d_h] row-major, rows padded by 32 bytes (conflict-free transposing
 //     reads, which hand the PV product its V^T operand directly).
+#include <type_traits>
+
 #include "internal.h"
 #include "mfma_common.h"
 
 namespace gqa {
 namespace {
 
-constexpr int kThreads = 512;   // 8 waves, 2 per SIMD
+constexpr int kThreads = 512;   // 8 waves: two groups of 4, one wave of each per SIMD
+constexpr int kGroup = 256;     // threads per group
 constexpr int kRowsWG = 256;    // query rows per workgroup (32 per wave)
 constexpr int kTile = 64;       // keys per tile
 
@@ -53,11 +67,12 @@ struct PrefillParams {
 
 template <int D>
 struct PrefillLds {
-  static constexpr int KS = D * 2 + 8;           // K row stride, bytes (8-byte reads conflict-free)
+  static constexpr int KS = D * 2 + 16;          // K row stride, bytes
   static constexpr int VS = D * 2 + 32;          // V row stride, bytes
-  static constexpr int K_BYTES = kTile * KS;
-  static constexpr int STAGE = K_BYTES + kTile * VS;
-  static constexpr int TOTAL = 2 * STAGE;
+  static constexpr int K_STAGE = kTile * KS;
+  static constexpr int V_STAGE = kTile * VS;
+  static constexpr int V_OFF = 2 * K_STAGE;      // two K stages, then two V stages
+  static constexpr int TOTAL = 2 * K_STAGE + 2 * V_STAGE;
 };
 
 template <int D, bool OUT_BF16>
@@ -68,7 +83,9 @@ prefill_bf16_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;     // 0: leads, streams K; 1: one phase behind, streams V
+  const int gtid = tid & (kGroup - 1);
   const int h = lane >> 5;       // lane half
   const int col = lane & 31;     // query row within the wave
 
@@ -120,65 +137,94 @@ prefill_bf16_kernel(PrefillParams p) {
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY;   // unscaled running maximum of this row
   float l_run = 0.f;         // this lane's share of the normalizer
+  f32x16 sacc[2];            // S^T of the current tile, two 32-key halves
+  bf16x8 pf[4];              // P^T of the previous tile, four 16-key chunks
 
+  // ---- staging: this group's tensor (K or V), global -> registers -> LDS
   const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
   const uint32_t slice_bytes = (uint32_t)kv_end * D * 2;     // keys >= kv_end read as zeros
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice_bytes);
-
-  // ---- tile loader: global -> registers -> LDS, 16 bytes per access
-  constexpr int UNITS = kTile * D / 8 / kThreads;          // 16-byte chunks per thread per tensor
-  uint4 kreg[UNITS], vreg[UNITS];
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc((grp == 0 ? p.k : p.v) + kv_base, slice_bytes);
+  const int s_stride = grp == 0 ? L::KS : L::VS;
+  unsigned char* const s_base = lds + (grp == 0 ? 0 : L::V_OFF);
+  const int s_stage = grp == 0 ? L::K_STAGE : L::V_STAGE;
+  constexpr int UNITS = kTile * D / 8 / kGroup;             // 16-byte chunks per thread
+  uint4 sreg[UNITS];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
-      const int u = tid + kThreads * i;
+      const int u = gtid + kGroup * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      const uint32_t off = (uint32_t)((t * kTile + row) * D + c8 * 8) * 2;
-      kreg[i] = load16(krs, off);
-      vreg[i] = load16(vrs, off);
+      sreg[i] = load16(srs, (uint32_t)((t * kTile + row) * D + c8 * 8) * 2);
     }
   };
-  auto store_tile = [&](int stage) {
-    unsigned char* ks_ = lds + stage * L::STAGE;
-    unsigned char* vs_ = ks_ + L::K_BYTES;
+  auto store_tile = [&](int t) {
+    unsigned char* dst = s_base + (t & 1) * s_stage;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
-      const int u = tid + kThreads * i;
+      const int u = gtid + kGroup * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      uint2* kd = reinterpret_cast<uint2*>(ks_ + row * L::KS + c8 * 16);   // rows are 8-byte aligned
-      kd[0] = make_uint2(kreg[i].x, kreg[i].y);
-      kd[1] = make_uint2(kreg[i].z, kreg[i].w);
-      *reinterpret_cast<uint4*>(vs_ + row * L::VS + c8 * 16) = vreg[i];
+      *reinterpret_cast<uint4*>(dst + row * s_stride + c8 * 16) = sreg[i];
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  // ---- staging duty of matrix phase t.  Leading group: K tile t + 1 to LDS, K tile
+  // t + 2 requested.  Trailing group: V tile t to LDS, V tile t + 1 requested.
+  // Each write goes to the stage whose previous tile both groups have finished.
+  auto stage_duty = [&](const int t) {
+    const int ts = grp == 0 ? t + 1 : t;
+    if (ts < n_tiles) {
+      store_tile(ts);
+      if (ts + 1 < n_tiles) load_tile(ts + 1);
+    }
+  };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    lds_barrier();
-
-    const unsigned char* ks_ = lds + (t & 1) * L::STAGE;
-    const unsigned char* vs_ = ks_ + L::K_BYTES;
-    const int k0 = t * kTile;
-
-    // S^T for the two 32-key halves of the tile
-    f32x16 sacc[2];
+  // ---- matrix phase t: O^T += V^T P^T for tile t - 1 (PV) and S^T = K Q^T for tile t
+  // (QK).  Operand reads run kWin ahead of the products that consume them, in an
+  // order pinned by scheduling barriers, alternating QK and PV products so that no
+  // accumulator is needed again before the product writing it has finished.
+  constexpr int NOP = D / 8;     // operands per product kind and tile
+  constexpr int kWin = 8;
+  constexpr int kStageAt = 8;    // staging duty is issued after this many products
+  auto matrix_phase = [&](const int t, auto qk_tag, auto pv_tag) {
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr int N = (QK ? NOP : 0) + (PV ? NOP : 0);
+    const unsigned char* ks_ = lds + (t & 1) * L::K_STAGE;
+    const unsigned char* vs_ = lds + L::V_OFF + ((t - 1) & 1) * L::V_STAGE;
+    auto is_pv = [&](int j) { return QK && PV ? (j & 1) != 0 : PV; };
+    auto idx = [&](int j) { return QK && PV ? j >> 1 : j; };
+    auto read = [&](int j) -> bf16x8 {
+      const int i = idx(j);
+      if (is_pv(j)) return load_vt_operand(vs_, L::VS, i / (D / 32), (i % (D / 32)) * 32, lane);
+      return *reinterpret_cast<const bf16x8*>(ks_ + ((i & 1) * 32 + col) * L::KS + ((i >> 1) * 16 + h * 8) * 2);
+    };
+    bf16x8 ops[kWin];
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
+    for (int j = 0; j < kWin && j < N; ++j) ops[j] = read(j);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = lds_read_bf16x8(ks_ + (kb * 32 + col) * L::KS + (kd * 16 + h * 8) * 2);
-        sacc[kb] = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
+    for (int j = 0; j < N; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = idx(j);
+      if (is_pv(j)) {
+        const int kc = i / (D / 32), db = i % (D / 32);
+        oacc[db] = mfma32(ops[j % kWin], pf[kc], oacc[db]);
+      } else {
+        const int kb = i & 1, kd = i >> 1;
+        sacc[kb] = mfma32(ops[j % kWin], qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
+      }
+      if (j + kWin < N) ops[j % kWin] = read(j + kWin);
+      if (j == kStageAt - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        stage_duty(t);
       }
     }
-    // keep four K operand reads in flight ahead of the products that consume them
-    sched_pipeline<D / 8, 2, 1, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
+  // ---- vector phase t: online-softmax update from S^T of tile t, P^T for the next
+  // matrix phase; then this group's staging duty: tile t + 1 to LDS, tile t + 2 requested
+  auto vector_phase = [&](const int t) {
+    const int k0 = t * kTile;
     // mask only where some key of the tile may be invisible to some row
     const bool need_mask = (p.causal && k0 + kTile - 1 > min_pos) || (k0 + kTile > len_b);
     if (need_mask) {
@@ -191,7 +237,6 @@ prefill_bf16_kernel(PrefillParams p) {
           sacc[kb][e] = vis ? sacc[kb][e] : -INFINITY;
         }
     }
-
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -210,7 +255,6 @@ prefill_bf16_kernel(PrefillParams p) {
       m_run = grow ? mx : m_run;
     }
     const float mc = (m_run == -INFINITY ? 0.f : m_run) * p.c;
-
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -221,26 +265,40 @@ prefill_bf16_kernel(PrefillParams p) {
         psum += pe;
       }
     l_run += psum;
-
-    // P^T fragments: chunk kc of the tile = elements 8*(kc&1) .. +7 of half kc>>1
-    bf16x8 pf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const f32x16& sv = sacc[kc >> 1];
       const int e0 = 8 * (kc & 1);
       pf[kc] = pack_bf16x8(sv[e0], sv[e0 + 1], sv[e0 + 2], sv[e0 + 3], sv[e0 + 4], sv[e0 + 5], sv[e0 + 6], sv[e0 + 7]);
     }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = load_vt_operand(vs_, L::VS, kc, db * 32, lane);
-        oacc[db] = mfma32(a, pf[kc], oacc[db]);
-      }
-    sched_pipeline<4 * D / 32, 2, 1, 4>();
+  };
 
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+  // ---- pipeline.  Phase k of the leading group runs beside phase k - 1 of the
+  // trailing one; both issue the same number of barriers.  K tile t is read in
+  // matrix phase t, V tile t in matrix phase t + 1; a stage is rewritten only
+  // after both groups are past its last reader.
+  if (n_tiles > 0) {
+    const auto yes = std::integral_constant<bool, true>{};
+    const auto no = std::integral_constant<bool, false>{};
+    load_tile(0);
+    if (grp == 0) {
+      store_tile(0);
+      if (n_tiles > 1) load_tile(1);
+    }
+    lds_barrier();
+    if (grp == 1) lds_barrier();   // the trailing group starts one phase late
+    matrix_phase(0, yes, no);
+    lds_barrier();
+    vector_phase(0);
+    lds_barrier();
+    for (int t = 1; t < n_tiles; ++t) {
+      matrix_phase(t, yes, yes);
+      lds_barrier();
+      vector_phase(t);
+      lds_barrier();
+    }
+    matrix_phase(n_tiles, no, yes);
+    if (grp == 0) lds_barrier();   // pairs with the trailing group's last barrier
   }
 
   // ---- epilogue: o = u / l
