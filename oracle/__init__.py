@@ -27,6 +27,8 @@ Modules:
   sdpa      -- the materialized definition O_a = softmax(Q_a K_g(a)^T * scale + M) V_g(a)
   online    -- the block-wise online-softmax state (m, l, u) and the merge of two states
   ledgers   -- the cache-byte, FLOP and arithmetic-intensity formulas
+  rope      -- rotary position encoding of query and key rows (the rotation is a
+               stated reading: the pages require it but print no formula)
 
 Every function is pinned by ``tests/test_oracle_*.py`` and ``tests/test_ledgers.py``
 against values the pages print, closed forms, invariants and brute force.
@@ -42,6 +44,7 @@ from .sdpa import (
 )
 from .online import online_states, online_attention_row, merge_states, finish_state
 from . import ledgers
+from .rope import rope, inv_freq
 
 __all__ = [
     "attention",
@@ -55,4 +58,6 @@ __all__ = [
     "merge_states",
     "finish_state",
     "ledgers",
+    "rope",
+    "inv_freq",
 ]
