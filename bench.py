@@ -224,6 +224,35 @@ def bench_decode(name, steps, warmup, flush_buf, page_size=0):
     return res, x
 
 
+# ---------------------------------------------------------------------------------------- rotary encoding
+def bench_rope(steps, warmup, flush_buf):
+    """Rotary encoding of the prefill workload's Q and K (out of place, bf16): HBM bytes
+    are the rows read plus the rows written."""
+    import torch
+
+    from grouped_query_attention_prefill_amd import inputs, ops
+
+    w = inputs.WORKLOADS["prefill_causal_bf16_T4096"]
+    q = torch.randn((w.B, w.h_q, w.T, w.d_h), device="cuda").to(torch.bfloat16)
+    k = torch.randn((w.B, w.h_kv, w.T, w.d_h), device="cuda").to(torch.bfloat16)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+
+    def fn():
+        ops.gqa_rope(q, out=qo)
+        ops.gqa_rope(k, out=ko)
+
+    log(f"[bench] timing rotary encoding of {w.name} Q and K")
+    wall, per = time_calls(fn, steps, warmup, flush=lambda: flush_buf.sum())
+    ms = sum(per) / len(per)
+    nbytes = 2 * (q.numel() + k.numel()) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name + "_qk_rope", "rows": w.B * (w.h_q + w.h_kv) * w.T, "d_h": w.d_h,
+            "algorithmic_bytes": nbytes, "ms_per_call": round(ms, 5), "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+            "kernels": "rope (Q) + rope (K)"}
+
+
 # ---------------------------------------------------------------------------------------- CPU oracle
 def cpu_baseline_prefill(res, min_s=10.0, max_s=30.0):
     """The float64 oracle on the prefill workload: whole query heads at full T, repeated
@@ -298,7 +327,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy", "rope"],
                     help="run one part alone (for profiler runs); prints that part's JSON")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -316,6 +345,10 @@ def main():
 
     if args.only == "copy":
         print(json.dumps(bench_copy(steps, warmup)), flush=True)
+        return
+    if args.only == "rope":
+        flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        print(json.dumps(bench_rope(steps, warmup, flush_buf)), flush=True)
         return
     if args.only == "prefill":
         r = bench_prefill(steps, warmup)
@@ -335,6 +368,7 @@ def main():
         for name, ps in SWEEP:
             r, _ = bench_decode(name, steps, warmup, flush_buf, ps)
             sweep.append(r)
+    rope = bench_rope(steps, warmup, flush_buf)
     del flush_buf
     torch.cuda.empty_cache()
 
@@ -360,6 +394,7 @@ def main():
                      "kernel_ms": round(pre["kernel_ms"], 5)},
         "decode": dec,
         "decode_sweep": sweep,
+        "rope": rope,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(pre)

@@ -199,6 +199,34 @@ int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const v
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int gqa_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, int d_h, float base,
+             int dtype, void* stream) {
+  if (B < 1 || H < 1 || S < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (d_h < 2 || d_h % 2 != 0 || d_h / 2 > gqa::kRopeMaxHalf) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(base) || base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+  const int eb = dtype == GQA_BF16 ? 2 : 4;
+  if (!x || !y || !aligned(x, eb) || !aligned(y, eb) || (pos0 && !aligned(pos0, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  return hip_status(gqa::launch_rope(x, y, pos0, B, H, S, d_h, base, eb, static_cast<hipStream_t>(stream)));
+}
+
+int gqa_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h, float base,
+                       int dtype, void* stream) {
+  if (B < 1 || h_kv < 1 || T_cap < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (d_h < 2 || d_h % 2 != 0 || d_h / 2 > gqa::kRopeMaxHalf) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(base) || base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+  const int eb = dtype == GQA_BF16 ? 2 : 4;
+  if (!k_cache || !v_cache || !k_new || !v_new || !write_pos) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_cache, eb) || !aligned(v_cache, eb) || !aligned(k_new, eb) || !aligned(v_new, eb) ||
+      !aligned(write_pos, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  return hip_status(gqa::launch_kv_append_rope(k_cache, v_cache, k_new, v_new, write_pos, B, h_kv, T_cap, d_h,
+                                               base, eb, static_cast<hipStream_t>(stream)));
+}
+
 int gqa_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                   const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h,
                   int dtype, void* stream) {

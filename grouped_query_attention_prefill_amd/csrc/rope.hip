@@ -1,0 +1,164 @@
+// Rotary position encoding of query and key rows, and the key-rotating append.
+//
+// Every query head and every stored key head is rotated by its position before
+// the scores are formed ([EffSeq] 分组查询注意力: under rotary encoding all query
+// heads and each key head actually kept are rotated; [MhaMqaGqa] note under the
+// parameter table: attention uses the position-processed Q and K).  A group's key
+// head is therefore rotated once, when it is written, not once per query head that
+// reads it; and the rotation is applied to the new key on its way into the cache,
+// never to rows already stored, which other readers may share ([Ch09] 09.4).
+//
+// The pages print no rotation formula; the form used is the common one, pair
+// (x[i], x[i + d/2]) turned by the angle p * theta_i, theta_i = base^(-2 i / d):
+//     y[i]       = x[i] cos - x[i + d/2] sin,   y[i + d/2] = x[i + d/2] cos + x[i] sin.
+// theta_i comes from the host in double precision, the angle p * theta_i is formed
+// and reduced to a fraction of a turn in double precision (angles reach 3e4
+// radians at the lengths served), and the hardware sine and cosine (which take
+// turns) are applied to that fraction in single precision.  Elements are read and
+// written in the tensor's own precision; the arithmetic is fp32.
+#include "internal.h"
+
+namespace gqa {
+namespace {
+
+struct RopeFreq {
+  double inv_freq[kRopeMaxHalf];   // theta_i, i < d / 2
+};
+
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(uint16_t* p, float v) {
+  const __bf16 b = (__bf16)v;                  // round to nearest even
+  *p = __builtin_bit_cast(uint16_t, b);
+}
+
+// cos and sin of p * theta: the angle is reduced in double precision to a fraction
+// of a turn in [-1/2, 1/2]; the hardware sine and cosine take that fraction.
+__device__ __forceinline__ void rot_cos_sin(int p, double theta, float& c, float& s) {
+  constexpr double kInv2Pi = 0.15915494309189533577;
+  const double turns = (double)p * theta * kInv2Pi;
+  const float f = (float)(turns - rint(turns));
+  c = __builtin_amdgcn_cosf(f);
+  s = __builtin_amdgcn_sinf(f);
+}
+
+template <typename T, int VEC>
+struct Vec;
+template <>
+struct Vec<float, 4> { typedef float4 type; };
+template <>
+struct Vec<uint16_t, 8> { typedef uint4 type; };
+template <typename T>
+struct Vec<T, 1> { typedef T type; };
+
+// One thread per (row, VEC consecutive pairs).  Rows are (b, h, s) of a (B, H, S, d)
+// tensor; row s of sequence b sits at position pos0[b] + s.  With VEC > 1 both halves
+// of the pairs move as 16-byte vectors.
+template <typename T, int VEC>
+__global__ void __launch_bounds__(256)
+rope_kernel(const T* x, T* y, const int32_t* pos0, int H, int S, int half, long long n_chunks, RopeFreq f) {
+  typedef typename Vec<T, VEC>::type V;
+  const long long cidx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (cidx >= n_chunks) return;
+  const int chunks = half / VEC;
+  const long long row = cidx / chunks;
+  const int i0 = (int)(cidx - row * chunks) * VEC;
+  const int s = (int)(row % S);
+  const int b = (int)(row / ((long long)S * H));
+  const int p = (pos0 ? pos0[b] : 0) + s;
+  const T* xr = x + row * 2 * half + i0;
+  T* yr = y + row * 2 * half + i0;
+  V lo = *reinterpret_cast<const V*>(xr);
+  V hi = *reinterpret_cast<const V*>(xr + half);
+  T* l = reinterpret_cast<T*>(&lo);
+  T* u = reinterpret_cast<T*>(&hi);
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float c, sn;
+    rot_cos_sin(p, f.inv_freq[i0 + v], c, sn);
+    const float x0 = ld(l + v), x1 = ld(u + v);
+    st(l + v, x0 * c - x1 * sn);
+    st(u + v, x1 * c + x0 * sn);
+  }
+  *reinterpret_cast<V*>(yr) = lo;
+  *reinterpret_cast<V*>(yr + half) = hi;
+}
+
+// Append with the key rotated at its own position: one workgroup per (K/V head,
+// sequence); threads < d/2 rotate key pairs, all threads copy the value row.
+template <typename T>
+__global__ void __launch_bounds__(128)
+kv_append_rope_kernel(T* kc, T* vc, const T* kn, const T* vn, const int32_t* write_pos, int h_kv,
+                      int T_cap, int half, RopeFreq f) {
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int wp = write_pos[b];
+  if (wp < 0 || wp >= T_cap) return;
+  const int d = 2 * half;
+  const T* ks = kn + (size_t)(b * h_kv + g) * d;
+  const T* vs = vn + (size_t)(b * h_kv + g) * d;
+  T* kd = kc + ((size_t)(b * h_kv + g) * T_cap + wp) * d;
+  T* vd = vc + ((size_t)(b * h_kv + g) * T_cap + wp) * d;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    float c, sn;
+    rot_cos_sin(wp, f.inv_freq[i], c, sn);
+    const float x0 = ld(ks + i), x1 = ld(ks + i + half);
+    st(kd + i, x0 * c - x1 * sn);
+    st(kd + i + half, x1 * c + x0 * sn);
+  }
+  for (int i = threadIdx.x; i < d; i += blockDim.x) vd[i] = vs[i];
+}
+
+RopeFreq make_freq(int d, float base) {
+  RopeFreq f;
+  const int half = d / 2;
+  for (int i = 0; i < kRopeMaxHalf; ++i)
+    f.inv_freq[i] = i < half ? std::pow((double)base, -2.0 * i / d) : 0.0;
+  return f;
+}
+
+}  // namespace
+
+hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, int D,
+                       float base, int elem_bytes, hipStream_t s) {
+  const int half = D / 2;
+  const long long n_rows = (long long)B * H * S;
+  const RopeFreq f = make_freq(D, base);
+  const bool al16 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+  const int vec = !al16 ? 1 : (elem_bytes == 4 ? (half % 4 == 0 ? 4 : 1) : (half % 8 == 0 ? 8 : 1));
+  const long long n_chunks = n_rows * (half / vec);
+  const long long blocks = (n_chunks + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (elem_bytes == 4) {
+    const float* xi = static_cast<const float*>(x);
+    float* yo = static_cast<float*>(y);
+    if (vec == 4) hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
+    else hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
+  } else {
+    const uint16_t* xi = static_cast<const uint16_t*>(x);
+    uint16_t* yo = static_cast<uint16_t*>(y);
+    if (vec == 8) hipLaunchKernelGGL((rope_kernel<uint16_t, 8>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
+    else hipLaunchKernelGGL((rope_kernel<uint16_t, 1>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                 const int32_t* write_pos, int B, int h_kv, int T_cap, int D, float base,
+                                 int elem_bytes, hipStream_t s) {
+  const RopeFreq f = make_freq(D, base);
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(kv_append_rope_kernel<float>, dim3(h_kv, B), dim3(128), 0, s,
+                       static_cast<float*>(k_cache), static_cast<float*>(v_cache), static_cast<const float*>(k_new),
+                       static_cast<const float*>(v_new), write_pos, h_kv, T_cap, D / 2, f);
+  else
+    hipLaunchKernelGGL(kv_append_rope_kernel<uint16_t>, dim3(h_kv, B), dim3(128), 0, s,
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), write_pos, h_kv,
+                       T_cap, D / 2, f);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -40,6 +40,8 @@ SIGNATURES = {
     "gqa_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gqa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "gqa_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "gqa_rope": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "gqa_kv_append_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -304,3 +306,41 @@ def gqa_kv_append_paged(k_pages, v_pages, k_new, v_new, block_table, write_pos):
                                    _ptr(write_pos), B, h_kv, page_size, n_pages, block_table.shape[1], d_h,
                                    _dtype_code(k_pages), _stream_handle(k_pages.device)))
     return k_pages, v_pages
+
+
+ROPE_BASE = 10000.0
+
+
+def gqa_rope(x, *, pos0=None, base: float = ROPE_BASE, out=None):
+    """Rotary encoding of x (B, H, S, d_h): row s of sequence b at position pos0[b] + s.
+
+    Returns ``out`` (a new tensor when None; pass ``out=x`` to rotate in place).
+    """
+    torch = _torch()
+    _dev_tensor(x, "x", 4)
+    B, H, S, d_h = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _dev_tensor(out, "out", 4)
+    _require(out.shape == x.shape and out.dtype == x.dtype, "out must match x")
+    pos0 = _int_vec(pos0, "pos0", B, x.device)
+    _check(load_library().gqa_rope(_ptr(x), _ptr(out), _ptr(pos0), B, H, S, d_h, float(base), _dtype_code(x),
+                                   _stream_handle(x.device)))
+    return out
+
+
+def gqa_kv_append_rope(k_cache, v_cache, k_new, v_new, write_pos, *, base: float = ROPE_BASE):
+    """kv_append with k_new rotated at position write_pos[b] (in place on the caches)."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, n, 4)
+    B, h_kv, T_cap, d_h = k_cache.shape
+    _require(v_cache.shape == k_cache.shape, "caches must match")
+    _require(tuple(k_new.shape) == (B, h_kv, 1, d_h) and k_new.shape == v_new.shape,
+             "k_new, v_new must be (B, h_kv, 1, d_h)")
+    _require(k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype, "dtypes must match")
+    write_pos = _int_vec(write_pos, "write_pos", B, k_cache.device)
+    _require(write_pos is not None, "write_pos is required")
+    _check(load_library().gqa_kv_append_rope(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                             _ptr(write_pos), B, h_kv, T_cap, d_h, float(base),
+                                             _dtype_code(k_cache), _stream_handle(k_cache.device)))
+    return k_cache, v_cache

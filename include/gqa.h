@@ -183,6 +183,40 @@ int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const v
                         const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
                         int page_size, int n_pages, int max_pages_per_seq, int d_h, int dtype, void* stream);
 
+/*
+ * Rotary position encoding.  Every query head and every stored key head is
+ * rotated by its position before scores are formed ([EffSeq] 分组查询注意力:
+ * all query heads and each key head actually kept are rotated; [MhaMqaGqa] note
+ * under the parameter table: attention uses the position-processed Q and K).
+ * The pages print no rotation formula; the one used is the common rotary form:
+ * element i of a head row is paired with element i + d_h/2 and the pair at
+ * position p is turned by p * theta_i, theta_i = base^(-2 i / d_h):
+ *     y[i] = x[i] cos - x[i + d_h/2] sin,   y[i + d_h/2] = x[i + d_h/2] cos + x[i] sin.
+ *
+ * gqa_rope: x, y (B, H, S, d_h) of `dtype`; row s of sequence b is at position
+ * pos0[b] + s (pos0 == NULL: s).  y may be x (in place); any other overlap is
+ * undefined.  Use it on Q (H = h_q) before gqa_prefill / gqa_prefill_chunk /
+ * gqa_decode, and on the prompt's K (H = h_kv) before it becomes the cache.
+ * Arithmetic is fp32 with angles reduced in double precision; bf16 results are
+ * rounded to nearest even.
+ * Errors: INVALID_ARGUMENT for a size < 1, a NULL or misaligned pointer, a base
+ * that is not finite or not > 1; UNSUPPORTED for an odd d_h, d_h > 256 or an
+ * unknown dtype.
+ */
+int gqa_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, int d_h, float base,
+             int dtype, void* stream);
+
+/*
+ * gqa_kv_append with the key rotated at its own position write_pos[b] on the way
+ * into the cache (values are copied unchanged).  Rows already in the cache are
+ * never touched: a cache that other readers share stays read-only to them
+ * ([Ch09] 09.4).  Arguments and skip rule as gqa_kv_append; base and errors as
+ * gqa_rope.
+ */
+int gqa_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h, float base,
+                       int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* gqa_status_string(int status);
 

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
-              "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged"):
+              "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged",
+              "gqa_rope", "gqa_kv_append_rope"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -123,3 +124,30 @@ def test_paged_validation():
     assert call(wsb=0) == ops.GQA_ERR_WORKSPACE_TOO_SMALL   # 32000 keys per sequence need splits
     assert lib.gqa_kv_append_paged(FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 2, 64, 10, 4, 128, 1, None) == ops.GQA_ERR_INVALID_ARGUMENT
     assert lib.gqa_kv_append_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 10, 4, 3, 1, None) == ops.GQA_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_rope_validation():
+    lib = ops.load_library()
+    ok = (FAKE, FAKE, None, 2, 8, 16, 128, 10000.0, ops.GQA_BF16, None)
+    def call(**kw):
+        names = ["x", "y", "pos0", "B", "H", "S", "d", "base", "dtype", "stream"]
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.gqa_rope(*a)
+    assert call(d=127) == ops.GQA_ERR_UNSUPPORTED                 # odd width
+    assert call(d=258) == ops.GQA_ERR_UNSUPPORTED                 # wider than 256
+    assert call(base=1.0) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(base=float("inf")) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(S=0) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(x=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(y=FAKE + 1) == ops.GQA_ERR_INVALID_ARGUMENT       # misaligned bf16
+    assert call(dtype=7) == ops.GQA_ERR_UNSUPPORTED
+    assert call(x=FAKE + 2, dtype=ops.GQA_F32) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_kv_append_rope(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 8, 64, 10000.0, 1, None) == \
+        ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 63, 10000.0, 1, None) == \
+        ops.GQA_ERR_UNSUPPORTED
+    assert lib.gqa_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 64, -1.0, 1, None) == \
+        ops.GQA_ERR_INVALID_ARGUMENT

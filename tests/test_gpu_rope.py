@@ -1,0 +1,163 @@
+"""GPU parity of rotary position encoding against the float64 oracle.
+
+gqa_rope and gqa_kv_append_rope are compared element by element with
+``oracle.rope`` on the same seeded inputs (fp32: absolute 1e-5; bf16 output:
+one bf16 unit in the last place of the expected value -- the output's rounding --
+plus 1e-6 of the pair's magnitude for the fp32 arithmetic, with nearly all
+elements within half a unit).  The end-to-end cases feed
+the rotated rows to prefill and decode and compare with the oracle's attention
+over the oracle's rotated rows, rounded to bf16 the way the kernel's inputs are.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from grouped_query_attention_prefill_amd import inputs, ops
+from tests.gpu_util import bf16_half_ulp, check_parity, f64, ints_dev, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_round(x64):
+    return inputs.f32_to_bf16_bits(np.asarray(x64, dtype=np.float32))
+
+
+def _pair_mag(x):
+    d = x.shape[-1]
+    m = np.abs(x[..., : d // 2]) + np.abs(x[..., d // 2:])
+    return np.concatenate([m, m], axis=-1)
+
+
+def _check_rope(got, want, dtype, what, x=None):
+    """fp32: absolute 1e-5.  bf16: within one bf16 ulp of the expected value plus the
+    fp32 arithmetic's share, 1e-6 of the pair's magnitude (that share decides the
+    rounding where the two terms of a rotated element cancel)."""
+    assert np.all(np.isfinite(got)), what
+    err = np.abs(got - want)
+    if dtype == "f32":
+        assert err.max() <= 1e-5, f"{what}: max-abs {err.max():.3g}"
+        return
+    hu = bf16_half_ulp(want)
+    slack = 1e-6 * _pair_mag(x) if x is not None else 0.0
+    assert np.all(err <= 2 * hu + slack), f"{what}: {np.max((err - slack) / hu):.3f} half-ulps"
+    assert np.mean(err <= hu + slack) > 0.999, f"{what}: too many results off the nearest bf16"
+
+
+ROPE_CASES = [
+    # dtype, B, H, S, d, pos0
+    ("bf16", 2, 8, 300, 128, [0, 31000]),
+    ("bf16", 1, 4, 64, 64, [12345]),
+    ("f32", 2, 3, 50, 40, [0, 32767]),
+    ("f32", 1, 2, 7, 2, None),
+    ("f32", 3, 2, 33, 256, [5, 0, 20000]),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: "%s_B%d_H%d_S%d_d%d" % c[:5])
+def test_rope_parity(case):
+    import torch
+
+    dt, B, H, S, d, pos0 = case
+    print(f"case rope {case[:5]}", flush=True)
+    x = inputs.normal(13000 + d, "q", (B, H, S, d), dt)
+    p0 = np.zeros(B, np.int64) if pos0 is None else np.asarray(pos0)
+    y = ops.gqa_rope(to_dev(x, dt), pos0=None if pos0 is None else ints_dev(pos0))
+    torch.cuda.synchronize()
+    want = oracle.rope(f64(x, dt), p0[:, None, None] + np.arange(S)[None, None, :])
+    _check_rope(to_host64(y), want, dt, str(case[:5]), x=f64(x, dt))
+
+
+def test_rope_in_place_equals_out_of_place():
+    import torch
+
+    x = inputs.normal(13100, "q", (2, 4, 100, 128), "bf16")
+    a = to_dev(x, "bf16")
+    b = ops.gqa_rope(a, pos0=ints_dev([7, 4000]))
+    ops.gqa_rope(a, pos0=ints_dev([7, 4000]), out=a)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_kv_append_rope(dt, d):
+    import torch
+
+    B, h_kv, T_cap = 4, 3, 40
+    k = inputs.normal(13200, "k", (B, h_kv, T_cap, d), dt)
+    v = inputs.normal(13200, "v", (B, h_kv, T_cap, d), dt)
+    kn = inputs.normal(13200, "k_new", (B, h_kv, 1, d), dt)
+    vn = inputs.normal(13200, "v_new", (B, h_kv, 1, d), dt)
+    wp = np.array([0, 39, 40, 17], np.int32)                 # 40 is out of range: skipped
+    kd, vd = to_dev(k, dt), to_dev(v, dt)
+    knd = to_dev(kn, dt)
+    ops.gqa_kv_append_rope(kd, vd, knd, to_dev(vn, dt), ints_dev(wp))
+    # the same rotation through gqa_rope (one row per sequence at write_pos)
+    ref = ops.gqa_rope(knd, pos0=ints_dev(wp))
+    torch.cuda.synchronize()
+    view = torch.int16 if dt == "bf16" else torch.int32
+    gk = kd.cpu()
+    gv = vd.cpu()
+    for b in range(B):
+        if not 0 <= wp[b] < T_cap:
+            continue
+        assert torch.equal(gk[b, :, wp[b]].view(view), ref.cpu()[b, :, 0].view(view))
+        want = oracle.rope(f64(kn[b, :, 0], dt), np.full(h_kv, wp[b]))
+        _check_rope(gk[b, :, wp[b]].float().numpy().astype(np.float64), want, dt, f"b={b}", x=f64(kn[b, :, 0], dt))
+        assert torch.equal(gv[b, :, wp[b]].view(view), torch.from_numpy(np.ascontiguousarray(vn[b, :, 0])).view(view)
+                           if dt == "f32" else torch.from_numpy(vn[b, :, 0].view(np.int16)))
+    # every other row untouched
+    mask = np.ones((B, T_cap), bool)
+    for b in range(B):
+        if 0 <= wp[b] < T_cap:
+            mask[b, wp[b]] = False
+    host_k = gk.view(view).numpy() if dt == "bf16" else gk.numpy().view(np.int32)
+    orig_k = k.view(np.int16) if dt == "bf16" else k.view(np.int32)
+    for b in range(B):
+        assert np.array_equal(host_k[b][:, mask[b]], orig_k[b][:, mask[b]])
+
+
+def test_rope_then_prefill():
+    import torch
+
+    B, h_q, h_kv, T, d = 1, 8, 2, 700, 128
+    x = inputs.make_prefill(B, h_q, h_kv, d, T, "bf16", 13300)
+    qd, kd, vd = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    o = ops.gqa_prefill(ops.gqa_rope(qd), ops.gqa_rope(kd), vd)
+    torch.cuda.synchronize()
+    pos = np.arange(T)
+    qr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(x["q"], "bf16"), pos))).astype(np.float64)
+    kr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(x["k"], "bf16"), pos))).astype(np.float64)
+    want = oracle.attention(qr, kr, f64(x["v"], "bf16"), causal=True)
+    check_parity(to_host64(o), want, mode="bf16", what="rope+prefill")
+
+
+def test_rope_append_decode():
+    # prompt keys rotated at their positions, the new key rotated inside the append,
+    # the query rotated at its absolute position, then decode
+    import torch
+
+    B, h_q, h_kv, d = 4, 16, 4, 128
+    T_cap = inputs.round_up(3000 + 1, 64)
+    x = inputs.make_append_decode(B, h_q, h_kv, d, T_cap, "bf16", 13400, hist_hi=3000)
+    hist = x["hist"]
+    k_hist = np.nan_to_num(f64(x["k_cache"], "bf16"))             # NaN rows beyond each history
+    kd = ops.gqa_rope(to_dev(x["k_cache"], "bf16"))               # whole cache, positions 0..T_cap-1
+    vd = to_dev(x["v_cache"], "bf16")
+    ops.gqa_kv_append_rope(kd, vd, to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints_dev(x["write_pos"]))
+    qd = ops.gqa_rope(to_dev(x["q"], "bf16"), pos0=ints_dev(x["q_pos"]))
+    o = ops.gqa_decode(qd, kd, vd, ints_dev(x["seq_lens"]), q_pos=ints_dev(x["q_pos"]),
+                       max_seq_len=int(x["seq_lens"].max()))
+    torch.cuda.synchronize()
+    got = to_host64(o)
+    for b in range(B):
+        L = int(x["seq_lens"][b])
+        k = k_hist[b:b + 1, :, :L].copy()
+        k[0, :, hist[b]] = f64(x["k_new"][b, :, 0], "bf16")
+        v = f64(x["v_cache"][b:b + 1, :, :L], "bf16").copy()
+        v[0, :, hist[b]] = f64(x["v_new"][b, :, 0], "bf16")
+        kr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(k, np.arange(L)))).astype(np.float64)
+        qr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(x["q"][b:b + 1], "bf16"),
+                                                             np.array([hist[b]])))).astype(np.float64)
+        want = oracle.attention(qr, kr, v, causal=True, q_pos=np.array([[hist[b]]]), kv_len=np.array([L]))
+        check_parity(got[b:b + 1], want, mode="bf16", what=f"rope decode b={b}")
