@@ -29,6 +29,8 @@ Modules:
   ledgers   -- the cache-byte, FLOP and arithmetic-intensity formulas
   rope      -- rotary position encoding of query and key rows (the rotation is a
                stated reading: the pages require it but print no formula)
+  backward  -- gradients dQ, dK, dV of the materialized attention (group heads
+               summed into their K/V head) and the saved row log-sum-exp
 
 Every function is pinned by ``tests/test_oracle_*.py`` and ``tests/test_ledgers.py``
 against values the pages print, closed forms, invariants and brute force.
@@ -45,6 +47,7 @@ from .sdpa import (
 from .online import online_states, online_attention_row, merge_states, finish_state
 from . import ledgers
 from .rope import rope, inv_freq
+from .backward import attention_backward, row_logsumexp
 
 __all__ = [
     "attention",
@@ -60,4 +63,6 @@ __all__ = [
     "ledgers",
     "rope",
     "inv_freq",
+    "attention_backward",
+    "row_logsumexp",
 ]
