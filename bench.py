@@ -224,6 +224,42 @@ def bench_decode(name, steps, warmup, flush_buf, page_size=0):
     return res, x
 
 
+# ---------------------------------------------------------------------------------------- backward
+def bench_backward(steps, warmup):
+    """Gradients of the prefill workload: delta, dK/dV and dQ kernels per call.
+
+    Algorithmic work: five products over the visible (query, key) pairs -- S, dP,
+    dV, dK, dQ -- 2 d_h FLOPs each per pair and query head, i.e. 2.5 times the
+    forward's 4 d_h; the second recomputation of S and dP is overhead, not counted.
+    """
+    import torch
+
+    from grouped_query_attention_prefill_amd import inputs, ops
+
+    w = inputs.WORKLOADS["prefill_causal_bf16_T4096"]
+    shape_q, shape_kv = (w.B, w.h_q, w.T, w.d_h), (w.B, w.h_kv, w.T, w.d_h)
+    q = torch.randn(shape_q, device="cuda").to(torch.bfloat16)
+    k = torch.randn(shape_kv, device="cuda").to(torch.bfloat16)
+    v = torch.randn(shape_kv, device="cuda").to(torch.bfloat16)
+    do = torch.randn(shape_q, device="cuda").to(torch.bfloat16)
+    o, lse = ops.gqa_prefill_lse(q, k, v)
+    dq = torch.empty(shape_q, dtype=torch.float32, device="cuda")
+    dk = torch.empty(shape_kv, dtype=torch.float32, device="cuda")
+    dv = torch.empty(shape_kv, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.gqa_prefill_backward_workspace_bytes(w.B, w.h_q, w.T), dtype=torch.uint8, device="cuda")
+    fn = lambda: ops.gqa_prefill_backward(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws)
+    log(f"[bench] timing the backward of {w.name}")
+    wall, per = time_calls(fn, steps, warmup)
+    ms = sum(per) / len(per)
+    flops = 10 * w.B * w.h_q * w.d_h * (w.T * (w.T + 1) // 2)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name + "_backward", "algorithmic_flops": flops, "ms_per_call": round(ms, 5),
+            "value": round(tf, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "kernels": "delta + dK/dV + dQ", "grad_dtype": "fp32"}
+
+
 # ---------------------------------------------------------------------------------------- rotary encoding
 def bench_rope(steps, warmup, flush_buf):
     """Rotary encoding of the prefill workload's Q and K (out of place, bf16): HBM bytes
@@ -327,7 +363,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy", "rope"],
+    ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy", "rope", "backward"],
                     help="run one part alone (for profiler runs); prints that part's JSON")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -345,6 +381,9 @@ def main():
 
     if args.only == "copy":
         print(json.dumps(bench_copy(steps, warmup)), flush=True)
+        return
+    if args.only == "backward":
+        print(json.dumps(bench_backward(steps, warmup)), flush=True)
         return
     if args.only == "rope":
         flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -369,6 +408,7 @@ def main():
             r, _ = bench_decode(name, steps, warmup, flush_buf, ps)
             sweep.append(r)
     rope = bench_rope(steps, warmup, flush_buf)
+    bwd = bench_backward(steps, warmup)
     del flush_buf
     torch.cuda.empty_cache()
 
@@ -395,6 +435,7 @@ def main():
         "decode": dec,
         "decode_sweep": sweep,
         "rope": rope,
+        "backward": bwd,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(pre)

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
 
-SOURCES = ["api.hip", "attn_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "kv_append.hip", "rope.hip"]
+SOURCES = ["api.hip", "attn_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "kv_append.hip", "rope.hip", "backward_bf16.hip"]
 ARCH = "gfx950"
 # packed fp32 vector instructions stay off: only plain fp32 VALU code is generated
 FLAGS = [

@@ -80,10 +80,9 @@ int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
   return run_attention(a, in_dtype, stream);
 }
 
-int gqa_prefill(const void* q, const void* k, const void* v, void* o,
-                int B, int h_q, int h_kv, int T, int d_h,
-                int mask, const int32_t* kv_lens, float scale,
-                int in_dtype, int out_dtype, void* stream) {
+static int prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int h_q, int h_kv, int T, int d_h, int mask, const int32_t* kv_lens, float scale,
+                        int in_dtype, int out_dtype, void* stream) {
   if (B < 1 || h_q < 1 || h_kv < 1 || T < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (mask != GQA_MASK_NONE && mask != GQA_MASK_CAUSAL) return GQA_ERR_INVALID_ARGUMENT;
@@ -94,6 +93,7 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o,
   st = check_ptrs(in_dtype, out_dtype, q, k, v, o);
   if (st != GQA_OK) return st;
   if (kv_lens && !aligned(kv_lens, 4)) return GQA_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return GQA_ERR_INVALID_ARGUMENT;
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.kv_lens = kv_lens; a.q_pos0 = nullptr;
@@ -102,7 +102,59 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o,
   a.q_pos_from_end = 0;    // query i sits at position i
   a.scale = scale;
   a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
+  a.lse = lse;
   return run_attention(a, in_dtype, stream);
+}
+
+int gqa_prefill(const void* q, const void* k, const void* v, void* o,
+                int B, int h_q, int h_kv, int T, int d_h,
+                int mask, const int32_t* kv_lens, float scale,
+                int in_dtype, int out_dtype, void* stream) {
+  return prefill_impl(q, k, v, o, nullptr, B, h_q, h_kv, T, d_h, mask, kv_lens, scale, in_dtype, out_dtype, stream);
+}
+
+int gqa_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int h_q, int h_kv, int T, int d_h,
+                    int mask, const int32_t* kv_lens, float scale,
+                    int in_dtype, int out_dtype, void* stream) {
+  if (!lse) return GQA_ERR_INVALID_ARGUMENT;
+  return prefill_impl(q, k, v, o, lse, B, h_q, h_kv, T, d_h, mask, kv_lens, scale, in_dtype, out_dtype, stream);
+}
+
+size_t gqa_prefill_backward_workspace_bytes(int B, int h_q, int T) {
+  if (B < 1 || h_q < 1 || T < 1) return 0;
+  return gqa::bwd_workspace_bytes(B, h_q, T);
+}
+
+int gqa_prefill_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                         const float* lse, float* dq, float* dk, float* dv,
+                         int B, int h_q, int h_kv, int T, int d_h, int mask, const int32_t* kv_lens,
+                         float scale, int in_dtype, int o_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || T < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (mask != GQA_MASK_NONE && mask != GQA_MASK_CAUSAL) return GQA_ERR_INVALID_ARGUMENT;
+  if (!scale_ok(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(in_dtype) || !known_dtype(o_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (in_dtype != GQA_BF16 || (d_h != 64 && d_h != 128)) return GQA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) ||
+      !aligned(o, o_dtype == GQA_BF16 ? 2 : 4) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || (kv_lens && !aligned(kv_lens, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  const size_t need = gqa::bwd_workspace_bytes(B, h_q, T);
+  if (workspace_bytes < need) return GQA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 4)) return GQA_ERR_INVALID_ARGUMENT;
+  gqa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.d_o = d_o; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.kv_lens = kv_lens;
+  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.T = T; a.D = d_h;
+  a.causal = mask == GQA_MASK_CAUSAL ? 1 : 0;
+  a.o_bf16 = o_dtype == GQA_BF16 ? 1 : 0;
+  a.scale = scale;
+  a.workspace = workspace;
+  return hip_status(gqa::launch_backward_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int T_cap, int d_h, int in_dtype) {

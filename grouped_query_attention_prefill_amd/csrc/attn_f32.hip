@@ -31,6 +31,7 @@ struct F32Params {
   const float* k;
   const float* v;
   float* o;
+  float* lse;             // (B, h_q, S_q) or null
   const int32_t* kv_lens;
   const int32_t* q_pos0;
   int h_q, h_kv, r, S_q, T_cap, D;
@@ -163,6 +164,8 @@ attn_f32_kernel(F32Params p) {
       const int d = rlane + 8 * e;
       if (d < D) orow[d] = u[e] * inv;
     }
+    // m is the running maximum of the scaled scores, l the sum of exp(s - m)
+    if (p.lse && rlane == 0) p.lse[(size_t)(b * p.h_q + head) * p.S_q + qi] = l > 0.f ? m + logf(l) : -INFINITY;
   }
 }
 
@@ -192,6 +195,7 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
   p.k = static_cast<const float*>(a.k);
   p.v = static_cast<const float*>(a.v);
   p.o = static_cast<float*>(a.o);
+  p.lse = a.lse;
   p.kv_lens = a.kv_lens;
   p.q_pos0 = a.q_pos0;
   p.h_q = a.h_q; p.h_kv = a.h_kv; p.r = a.h_q / a.h_kv;
@@ -207,6 +211,7 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
   p.k = static_cast<const float*>(a.k);
   p.v = static_cast<const float*>(a.v);
   p.o = static_cast<float*>(a.o);
+  p.lse = nullptr;
   p.kv_lens = a.seq_lens;
   p.q_pos0 = a.q_pos;
   p.h_q = a.h_q; p.h_kv = a.h_kv; p.r = a.h_q / a.h_kv;

@@ -1,0 +1,502 @@
+// Gradients of bf16 grouped-query prefill attention on the gfx950 matrix cores:
+// dQ, dK, dV in fp32 from Q, K, V, the forward output O, its gradient dO and the
+// row log-sum-exp L the forward saved.
+//
+// Method ([EffSeq] 在线 softmax: the forward keeps only per-row statistics, so
+// probabilities are recomputed; [AttnVar] 3.5: tiles are recomputed instead of
+// storing the T x T matrices).  With s = scale * q k and P = exp(s - L):
+//     delta_i = sum_d dO_id O_id                       (one pass over O and dO)
+//     dV_j    = sum_i P_ij dO_i
+//     dS_ij   = P_ij (dO_i . V_j - delta_i)
+//     dQ_i    = scale * sum_j dS_ij K_j
+//     dK_j    = scale * sum_i dS_ij Q_i
+// Every query head a of a group adds into the gradients of K/V head g(a)
+// ([EffSeq] 分组查询注意力: r query heads read one K/V head).  The sums over the
+// group stay inside one workgroup, so no atomics are used and results do not
+// depend on scheduling.
+//
+// Two kernels recompute the probabilities independently:
+//   dK/dV: a workgroup owns 64 keys of one (sequence, K/V head); each wave owns
+//     32 of them, their K and V rows held in registers, and walks the 32-row query
+//     tiles of every query head in the group that can see those keys.  Per tile:
+//     S = Q K^T and dP = dO V^T (rows = queries, one key per lane column), then
+//     dV^T += dO^T P and dK^T += Q^T dS with P and dS straight from registers and
+//     dO^T, Q^T read transposed from LDS.  Waves of the two query-tile parities
+//     add their partial sums at the end.
+//   dQ: a workgroup owns 128 query rows (heads x positions of one group, as in
+//     the forward); Q and dO rows stay in registers and 64-key tiles of K and V
+//     stream through LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+#include "internal.h"
+#include "mfma_common.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kBwdThreads = 256;   // 4 waves
+constexpr int kKeyBlock = 64;      // keys per dK/dV workgroup
+constexpr int kQTile = 32;         // query rows per dK/dV tile
+constexpr int kDqRows = 128;       // query rows per dQ workgroup
+constexpr int kDqTile = 64;        // keys per dQ tile
+
+struct BwdParams {
+  const uint16_t* q;       // (B, h_q, T, D) bf16
+  const uint16_t* k;       // (B, h_kv, T, D)
+  const uint16_t* v;
+  const void* o;           // (B, h_q, T, D) fp32 or bf16
+  const uint16_t* d_o;     // (B, h_q, T, D) bf16
+  const float* lse;        // (B, h_q, T)
+  float* delta;            // (B, h_q, T) workspace
+  float* dq;               // (B, h_q, T, D) fp32
+  float* dk;               // (B, h_kv, T, D) fp32
+  float* dv;
+  const int32_t* kv_lens;
+  int B, h_q, h_kv, r, T, causal, o_bf16;
+  int hp, P, n_qblocks, n_hchunks;   // dQ row packing (as the forward)
+  float scale, c;                    // c = scale * log2(e)
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// ---------------------------------------------------------------------------
+// delta_i = sum_d dO_id O_id: one wave per row
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_delta_kernel(BwdParams p) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const long long n_rows = (long long)p.B * p.h_q * p.T;
+  if (row >= n_rows) return;
+  float acc = 0.f;
+  for (int d = lane; d < D; d += 64) {
+    const float o = p.o_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.o)[row * D + d])
+                             : static_cast<const float*>(p.o)[row * D + d];
+    acc = fmaf(bf16_to_f32(p.d_o[row * D + d]), o, acc);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) p.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkdvLds {
+  static constexpr int TS = D * 2 + 32;            // tile row stride (transposing reads conflict-free)
+  static constexpr int TILE = kQTile * TS;
+  static constexpr int REGION = 2 * TILE + 2 * kQTile * 4;   // Q tile, dO tile, L, delta
+  static constexpr int STAGING = 2 * 2 * REGION;             // two parities x two stages
+  static constexpr int REDUCE = 2 * 2 * (D / 32) * 16 * 64 * 4;   // two waves x (dK, dV) accumulators
+  static constexpr int TOTAL = STAGING > REDUCE ? STAGING : REDUCE;
+};
+
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads, 1)
+bwd_dkdv_kernel(BwdParams p) {
+  using L = DkdvLds<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 1;          // key half of the block
+  const int qw = wave >> 1;         // query-tile parity
+  const int h = lane >> 5, col = lane & 31;
+  const int gtid = tid & 127;       // thread index within the parity pair
+
+  // heaviest key blocks first: under a causal mask the first keys are seen by every row
+  const int n_bg = p.B * p.h_kv;
+  const int kb = blockIdx.x / n_bg;
+  const int bg = blockIdx.x % n_bg;
+  const int g = bg % p.h_kv, b = bg / p.h_kv;
+  const int len_b = clampi(p.kv_lens ? p.kv_lens[b] : p.T, 0, p.T);
+  const int key0 = kb * kKeyBlock + kw * 32;        // first key of this wave
+  const int key = key0 + col;                       // this lane's key
+
+  // K and V rows of this wave's keys: B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const size_t base = ((size_t)(b * p.h_kv + g) * p.T + key) * D;
+    const bool ok = key < len_b;
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd) {
+      uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+      if (ok) {
+        x = *reinterpret_cast<const uint4*>(p.k + base + kd * 16 + h * 8);
+        y = *reinterpret_cast<const uint4*>(p.v + base + kd * 16 + h * 8);
+      }
+      kf[kd] = __builtin_bit_cast(bf16x8, x);
+      vf[kd] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dkacc[db][e] = 0.f; dvacc[db][e] = 0.f; }
+
+  // query tiles that can see some key of the block: every head of the group, rows
+  // from the block's first key on (causal) or all rows
+  const int n_qt = (p.T + kQTile - 1) / kQTile;
+  const int qt0 = (p.causal && kb * kKeyBlock < len_b) ? (kb * kKeyBlock) / kQTile : 0;
+  const int per_head = n_qt - qt0;
+  const int n_items = (kb * kKeyBlock < len_b) ? p.r * per_head : 0;
+  const int n_steps = (n_items + 1) / 2;
+
+  // staging of one item (head, query tile) into region (qw, stage) by the two waves of parity qw
+  constexpr int UNITS = kQTile * D / 8 / 128;        // 16-byte chunks per thread per tensor
+  uint4 qreg[UNITS], oreg[UNITS];
+  float lreg = 0.f, dreg = 0.f;
+  auto item_of = [&](int it, int& head, int& qt) {
+    head = g * p.r + it / per_head;
+    qt = qt0 + it % per_head;
+  };
+  auto load_item = [&](int it) {
+    if (it >= n_items) return;
+    int head, qt;
+    item_of(it, head, qt);
+    const size_t rbase = ((size_t)(b * p.h_q + head) * p.T) * D;
+    const uint32_t bytes = (uint32_t)p.T * D * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + rbase, bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.d_o + rbase, bytes);
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = gtid + 128 * i;
+      const int row = u / (D / 8), c8 = u % (D / 8);
+      const uint32_t off = (uint32_t)(((qt * kQTile + row) * D + c8 * 8) * 2);
+      qreg[i] = load16(qr, off);
+      oreg[i] = load16(dr, off);
+    }
+    const int qi = qt * kQTile + (gtid & 31);
+    const size_t li = (size_t)(b * p.h_q + head) * p.T + qi;
+    if (gtid < 32) lreg = qi < p.T ? p.lse[li] : -INFINITY;
+    else if (gtid < 64) dreg = qi < p.T ? p.delta[li] : 0.f;
+  };
+  auto region = [&](int par, int stage) { return lds + (par * 2 + stage) * L::REGION; };
+  auto store_item = [&](int it, int stage) {
+    if (it >= n_items) return;
+    unsigned char* rg = region(qw, stage);
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = gtid + 128 * i;
+      const int row = u / (D / 8), c8 = u % (D / 8);
+      *reinterpret_cast<uint4*>(rg + row * L::TS + c8 * 16) = qreg[i];
+      *reinterpret_cast<uint4*>(rg + L::TILE + row * L::TS + c8 * 16) = oreg[i];
+    }
+    float* lv = reinterpret_cast<float*>(rg + 2 * L::TILE);
+    if (gtid < 32) lv[gtid] = lreg;
+    else if (gtid < 64) lv[kQTile + (gtid - 32)] = dreg;
+  };
+
+  // one item on this wave: 32 query rows x 32 keys, 32 products
+  auto compute_item = [&](int it, int stage) {
+    int head, qt;
+    item_of(it, head, qt);
+    (void)head;
+    const unsigned char* rg = region(qw, stage);
+    const unsigned char* qs = rg;
+    const unsigned char* os = rg + L::TILE;
+    const float* lv = reinterpret_cast<const float*>(rg + 2 * L::TILE);
+    f32x16 sacc, dpacc;
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qs + col * L::TS + (kd * 16 + h * 8) * 2);
+      const bf16x8 o = *reinterpret_cast<const bf16x8*>(os + col * L::TS + (kd * 16 + h * 8) * 2);
+      sacc = mfma32(a, kf[kd], kd == 0 ? f32x16{} : sacc);
+      dpacc = mfma32(o, vf[kd], kd == 0 ? f32x16{} : dpacc);
+    }
+    // rows of element e: query 8 (e / 4) + 4 h + e % 4 of the tile; column: this lane's key
+    const int q0 = qt * kQTile;
+    const bool edge = (p.causal && key0 + 31 > q0) || (key0 + 32 > len_b) || (q0 + kQTile > p.T);
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lv + 8 * jq + 4 * h);
+      const float4 d4 = *reinterpret_cast<const float4*>(lv + kQTile + 8 * jq + 4 * h);
+      const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dq4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * jq + i;
+        const int qrow = q0 + 8 * jq + 4 * h + i;
+        bool vis = lq[i] != -INFINITY;
+        if (edge) vis = vis && key < len_b && qrow < p.T && (!p.causal || key <= qrow);
+        const float pr = vis ? fast_exp2(fmaf(sacc[e], p.c, -lq[i] * kLog2e)) : 0.f;
+        sacc[e] = pr;
+        dpacc[e] = pr * (dpacc[e] - dq4[i]);
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int e0 = 8 * kc;
+      pf[kc] = pack_bf16x8(sacc[e0], sacc[e0 + 1], sacc[e0 + 2], sacc[e0 + 3], sacc[e0 + 4], sacc[e0 + 5],
+                           sacc[e0 + 6], sacc[e0 + 7]);
+      dsf[kc] = pack_bf16x8(dpacc[e0], dpacc[e0 + 1], dpacc[e0 + 2], dpacc[e0 + 3], dpacc[e0 + 4],
+                            dpacc[e0 + 5], dpacc[e0 + 6], dpacc[e0 + 7]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS; operands read transposed in the row order
+    // the accumulator layout hands P and dS over in
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 ot = load_vt_operand(os, L::TS, kc, db * 32, lane);
+        const bf16x8 qt_ = load_vt_operand(qs, L::TS, kc, db * 32, lane);
+        dvacc[db] = mfma32(ot, pf[kc], dvacc[db]);
+        dkacc[db] = mfma32(qt_, dsf[kc], dkacc[db]);
+      }
+  };
+
+  // ---- pipeline: step s handles items 2s (parity 0) and 2s + 1 (parity 1)
+  load_item(2 * 0 + qw);
+  store_item(qw, 0);
+  lds_barrier();
+  for (int s = 0; s < n_steps; ++s) {
+    const int it = 2 * s + qw;
+    if (s + 1 < n_steps) load_item(it + 2);
+    if (it < n_items) compute_item(it, s & 1);
+    if (s + 1 < n_steps) store_item(it + 2, (s + 1) & 1);
+    lds_barrier();
+  }
+
+  // ---- add the two parities' partial sums, then write dK = scale dK^T^T and dV
+  float* red = reinterpret_cast<float*>(lds);      // [kw][dk | dv][db][e][lane]
+  if (qw == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red[(((kw * 2 + 0) * (D / 32) + db) * 16 + e) * 64 + lane] = dkacc[db][e];
+        red[(((kw * 2 + 1) * (D / 32) + db) * 16 + e) * 64 + lane] = dvacc[db][e];
+      }
+  }
+  lds_barrier();
+  if (qw == 0 && key < p.T) {
+    const size_t obase = ((size_t)(b * p.h_kv + g) * p.T + key) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float kk[4], vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * j + i;
+          kk[i] = (dkacc[db][e] + red[(((kw * 2 + 0) * (D / 32) + db) * 16 + e) * 64 + lane]) * p.scale;
+          vv[i] = dvacc[db][e] + red[(((kw * 2 + 1) * (D / 32) + db) * 16 + e) * 64 + lane];
+        }
+        const int d0 = db * 32 + 8 * j + 4 * h;
+        *reinterpret_cast<float4*>(p.dk + obase + d0) = make_float4(kk[0], kk[1], kk[2], kk[3]);
+        *reinterpret_cast<float4*>(p.dv + obase + d0) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqLds {
+  static constexpr int KTS = D * 2 + 32;           // K tile: read as rows and transposed
+  static constexpr int VTS = D * 2 + 16;           // V tile: read as rows
+  static constexpr int K_BYTES = kDqTile * KTS;
+  static constexpr int STAGE = K_BYTES + kDqTile * VTS;
+  static constexpr int TOTAL = 2 * STAGE;
+};
+
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads, 1)
+bwd_dq_kernel(BwdParams p) {
+  using L = DqLds<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+
+  // heaviest query blocks first (as the forward)
+  const int bgh = blockIdx.x / p.n_qblocks;
+  const int qb = p.n_qblocks - 1 - (blockIdx.x % p.n_qblocks);
+  const int hc = bgh % p.n_hchunks;
+  const int bg = bgh / p.n_hchunks;
+  const int g = bg % p.h_kv, b = bg / p.h_kv;
+  const int len_b = clampi(p.kv_lens ? p.kv_lens[b] : p.T, 0, p.T);
+
+  const int rho = wave * 32 + col;
+  const int head = g * p.r + hc * p.hp + rho / p.P;
+  const int qi = qb * p.P + rho % p.P;
+  const bool row_valid = qi < p.T;
+  const size_t rrow = (size_t)(b * p.h_q + head) * p.T + qi;
+
+  bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+  for (int kd = 0; kd < D / 16; ++kd) {
+    uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+    if (row_valid) {
+      x = *reinterpret_cast<const uint4*>(p.q + rrow * D + kd * 16 + h * 8);
+      y = *reinterpret_cast<const uint4*>(p.d_o + rrow * D + kd * 16 + h * 8);
+    }
+    qf[kd] = __builtin_bit_cast(bf16x8, x);
+    of[kd] = __builtin_bit_cast(bf16x8, y);
+  }
+  const float lrow = row_valid ? p.lse[rrow] : -INFINITY;
+  const float drow = row_valid ? p.delta[rrow] : 0.f;
+  const float lc = lrow * kLog2e;
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqacc[db][e] = 0.f;
+
+  const int first_q = qb * p.P;
+  const int last_q = min(first_q + p.P, p.T) - 1;
+  const int kv_end = p.causal ? min(len_b, last_q + 1) : len_b;
+  const int n_tiles = (kv_end + kDqTile - 1) / kDqTile;
+
+  const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T * D;
+  const uint32_t slice = (uint32_t)kv_end * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice);
+  constexpr int UNITS = kDqTile * D / 8 / kBwdThreads;
+  uint4 kreg[UNITS], vreg[UNITS];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = tid + kBwdThreads * i;
+      const int row = u / (D / 8), c8 = u % (D / 8);
+      const uint32_t off = (uint32_t)((t * kDqTile + row) * D + c8 * 8) * 2;
+      kreg[i] = load16(krs, off);
+      vreg[i] = load16(vrs, off);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    unsigned char* ks_ = lds + stage * L::STAGE;
+    unsigned char* vs_ = ks_ + L::K_BYTES;
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = tid + kBwdThreads * i;
+      const int row = u / (D / 8), c8 = u % (D / 8);
+      *reinterpret_cast<uint4*>(ks_ + row * L::KTS + c8 * 16) = kreg[i];
+      *reinterpret_cast<uint4*>(vs_ + row * L::VTS + c8 * 16) = vreg[i];
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    lds_barrier();
+    const unsigned char* ks_ = lds + (t & 1) * L::STAGE;
+    const unsigned char* vs_ = ks_ + L::K_BYTES;
+    const int k0 = t * kDqTile;
+    f32x16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks_ + (kb * 32 + col) * L::KTS + (kd * 16 + h * 8) * 2);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(vs_ + (kb * 32 + col) * L::VTS + (kd * 16 + h * 8) * 2);
+        sacc[kb] = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
+        dpacc[kb] = mfma32(v, of[kd], kd == 0 ? f32x16{} : dpacc[kb]);
+      }
+    // rows of element e: key k0 + 32 kb + 8 (e / 4) + 4 h + e % 4; column: this lane's query
+    const bool edge = (p.causal && k0 + kDqTile - 1 > first_q) || (k0 + kDqTile > len_b);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        bool vis = lrow != -INFINITY;
+        if (edge) vis = vis && kk < len_b && (!p.causal || kk <= qi);
+        const float pr = vis ? fast_exp2(fmaf(sacc[kb][e], p.c, -lc)) : 0.f;
+        dpacc[kb][e] = pr * (dpacc[kb][e] - drow);
+      }
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const f32x16& sv = dpacc[kc >> 1];
+      const int e0 = 8 * (kc & 1);
+      dsf[kc] = pack_bf16x8(sv[e0], sv[e0 + 1], sv[e0 + 2], sv[e0 + 3], sv[e0 + 4], sv[e0 + 5], sv[e0 + 6],
+                            sv[e0 + 7]);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 a = load_vt_operand(ks_, L::KTS, kc, db * 32, lane);
+        dqacc[db] = mfma32(a, dsf[kc], dqacc[db]);
+      }
+    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+  }
+
+  if (row_valid) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = db * 32 + 8 * j + 4 * h;
+        *reinterpret_cast<float4*>(p.dq + rrow * D + d0) =
+            make_float4(dqacc[db][4 * j] * p.scale, dqacc[db][4 * j + 1] * p.scale, dqacc[db][4 * j + 2] * p.scale,
+                        dqacc[db][4 * j + 3] * p.scale);
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_t(const BwdParams& prm, hipStream_t s) {
+  const long long rows = (long long)prm.B * prm.h_q * prm.T;
+  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  static bool attr = false;
+  if (!attr) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, DkdvLds<D>::TOTAL);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel<D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, DqLds<D>::TOTAL);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int n_kb = (prm.T + kKeyBlock - 1) / kKeyBlock;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(prm.B * prm.h_kv * n_kb)), dim3(kBwdThreads),
+                     DkdvLds<D>::TOTAL, s, prm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long n_dq = (long long)prm.B * prm.h_kv * prm.n_hchunks * prm.n_qblocks;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(kBwdThreads), DqLds<D>::TOTAL, s, prm);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int h_q, int T) { return (size_t)B * h_q * T * sizeof(float); }
+
+hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t s) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = a.o;
+  p.d_o = static_cast<const uint16_t*>(a.d_o);
+  p.lse = a.lse;
+  p.delta = static_cast<float*>(a.workspace);
+  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv;
+  p.kv_lens = a.kv_lens;
+  p.B = a.B; p.h_q = a.h_q; p.h_kv = a.h_kv; p.r = a.h_q / a.h_kv; p.T = a.T;
+  p.causal = a.causal; p.o_bf16 = a.o_bf16;
+  int hp = 1;
+  while (hp < kDqRows && p.r % (hp * 2) == 0) hp *= 2;
+  p.hp = hp;
+  p.P = kDqRows / hp;
+  p.n_qblocks = (a.T + p.P - 1) / p.P;
+  p.n_hchunks = p.r / hp;
+  p.scale = a.scale;
+  p.c = a.scale * kLog2e;
+  const long long n_dq = (long long)a.B * a.h_kv * p.n_hchunks * p.n_qblocks;
+  const long long n_kv = (long long)a.B * a.h_kv * ((a.T + kKeyBlock - 1) / kKeyBlock);
+  if (n_dq > 0x7fffffffLL || n_kv > 0x7fffffffLL || (long long)a.B * a.h_q * a.T / 4 + 1 > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  return a.D == 128 ? launch_t<128>(p, s) : launch_t<64>(p, s);
+}
+
+}  // namespace gqa

@@ -22,6 +22,7 @@ struct AttnArgs {
   int q_pos_from_end;     // 1: default position of row 0 is kv_len - S_q
   float scale;
   int out_bf16;           // output dtype of the bf16 path
+  float* lse = nullptr;   // (B, h_q, S_q) natural-log row log-sum-exp of the scaled scores, or null
 };
 
 // Decode: one query per sequence at q_pos[b] (null -> seq_lens[b] - 1), keys
@@ -62,6 +63,26 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStrea
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* write_pos, int B, int h_kv, int T_cap, int D,
                             int elem_bytes, hipStream_t s);
+// Gradients of bf16 prefill attention (dQ, dK, dV in fp32) from the forward's output
+// O and row log-sum-exp; the workspace holds delta = rowsum(dO * O), one float per row.
+struct BwdArgs {
+  const void* q;          // (B, h_q, T, D) bf16
+  const void* k;          // (B, h_kv, T, D) bf16
+  const void* v;
+  const void* o;          // (B, h_q, T, D) fp32 or bf16 (o_bf16)
+  const void* d_o;        // (B, h_q, T, D) bf16
+  const float* lse;       // (B, h_q, T)
+  float* dq;              // (B, h_q, T, D)
+  float* dk;              // (B, h_kv, T, D)
+  float* dv;
+  const int32_t* kv_lens; // (B,) or null -> T
+  int B, h_q, h_kv, T, D, causal, o_bf16;
+  float scale;
+  void* workspace;        // bwd_workspace_bytes(B, h_q, T)
+};
+size_t bwd_workspace_bytes(int B, int h_q, int T);
+hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t s);
+
 // rotary encoding: head widths up to 2 * kRopeMaxHalf
 constexpr int kRopeMaxHalf = 128;
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, int D,

@@ -55,6 +55,7 @@ struct PrefillParams {
   const uint16_t* k;
   const uint16_t* v;
   void* o;
+  float* lse;                   // (B, h_q, S_q) row log-sum-exp, or null
   const int32_t* kv_lens;
   const int32_t* q_pos0;
   int h_q, h_kv, r, hp, P;      // hp heads x P positions = 256 rows per workgroup
@@ -63,6 +64,7 @@ struct PrefillParams {
   int n_qblocks, n_hchunks;
   int xcd_remap;
   float c;                      // scale * log2(e)
+  float scale;
 };
 
 template <int D>
@@ -357,6 +359,10 @@ prefill_bf16_kernel(PrefillParams p) {
   // ---- epilogue: o = u / l
   const float l_tot = pair_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (row_valid && p.lse && h == 0) {
+    // l_tot sums exp(scale (s - m)) with m the unscaled running maximum
+    p.lse[(size_t)(b * p.h_q + head) * p.S_q + qi] = l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+  }
   if (row_valid) {
     const size_t obase = ((size_t)(b * p.h_q + head) * p.S_q + qi) * D;
 #pragma unroll
@@ -400,6 +406,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
   p.o = a.o;
+  p.lse = a.lse;
   p.kv_lens = a.kv_lens;
   p.q_pos0 = a.q_pos0;
   p.h_q = a.h_q; p.h_kv = a.h_kv; p.r = a.h_q / a.h_kv;
@@ -413,6 +420,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   p.n_qblocks = (a.S_q + p.P - 1) / p.P;
   p.n_hchunks = p.r / hp;
   p.c = a.scale * kLog2e;
+  p.scale = a.scale;
   const long long total = (long long)a.B * a.h_kv * p.n_hchunks * p.n_qblocks;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;

@@ -42,6 +42,10 @@ SIGNATURES = {
     "gqa_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_rope": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_kv_append_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "gqa_prefill_lse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P]),
+    "gqa_prefill_backward_workspace_bytes": (_S, [_I, _I, _I]),
+    "gqa_prefill_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I, _I,
+                                  _P, _S, _P]),
     "gqa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -344,3 +348,71 @@ def gqa_kv_append_rope(k_cache, v_cache, k_new, v_new, write_pos, *, base: float
                                              _ptr(write_pos), B, h_kv, T_cap, d_h, float(base),
                                              _dtype_code(k_cache), _stream_handle(k_cache.device)))
     return k_cache, v_cache
+
+
+def gqa_prefill_lse(q, k, v, *, causal: bool = True, scale: Optional[float] = None, kv_lens=None,
+                    out=None, out_dtype=None, lse=None):
+    """gqa_prefill that also returns the row log-sum-exp (B, h_q, T) fp32 a backward pass needs."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, n, 4)
+    B, h_q, T, d_h = q.shape
+    _require(k.shape == v.shape and k.shape[0] == B and k.shape[2] == T and k.shape[3] == d_h,
+             "k, v must be (B, h_kv, T, d_h) matching q")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    h_kv = k.shape[1]
+    code = _dtype_code(q)
+    oc = _out_code(code, out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((B, h_q, T, d_h), dtype=_torch_dtype(oc), device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h_q, T), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, "out", 4)
+    _dev_tensor(lse, "lse", 3)
+    _require(lse.dtype == torch.float32 and tuple(lse.shape) == (B, h_q, T), "lse must be fp32 (B, h_q, T)")
+    kv_lens = _int_vec(kv_lens, "kv_lens", B, q.device)
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    _check(load_library().gqa_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, h_q, h_kv, T, d_h,
+                                          GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc,
+                                          code, oc, _stream_handle(q.device)))
+    return out, lse
+
+
+def gqa_prefill_backward_workspace_bytes(B: int, h_q: int, T: int) -> int:
+    return int(load_library().gqa_prefill_backward_workspace_bytes(B, h_q, T))
+
+
+def gqa_prefill_backward(q, k, v, o, d_o, lse, *, causal: bool = True, scale: Optional[float] = None,
+                         kv_lens=None, dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV (fp32) of bf16 prefill attention from O, dO and the forward's row log-sum-exp."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+        _dev_tensor(t, n, 4)
+    B, h_q, T, d_h = q.shape
+    h_kv = k.shape[1]
+    _require(k.shape == v.shape and tuple(k.shape) == (B, h_kv, T, d_h), "k, v must be (B, h_kv, T, d_h)")
+    _require(o.shape == q.shape and d_o.shape == q.shape, "o and d_o must match q")
+    _require(q.dtype == k.dtype == v.dtype == d_o.dtype, "q, k, v, d_o must share a dtype")
+    _dev_tensor(lse, "lse", 3)
+    _require(lse.dtype == torch.float32 and tuple(lse.shape) == (B, h_q, T), "lse must be fp32 (B, h_q, T)")
+    if dq is None:
+        dq = torch.empty((B, h_q, T, d_h), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, h_kv, T, d_h), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, h_kv, T, d_h), dtype=torch.float32, device=q.device)
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _dev_tensor(t, n, 4)
+        _require(t.dtype == torch.float32, f"{n} must be fp32")
+    kv_lens = _int_vec(kv_lens, "kv_lens", B, q.device)
+    lib = load_library()
+    ws_bytes = int(lib.gqa_prefill_backward_workspace_bytes(B, h_q, T))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = workspace.numel() * workspace.element_size()
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    _check(lib.gqa_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, h_q, h_kv, T, d_h, GQA_MASK_CAUSAL if causal else GQA_MASK_NONE,
+                                    _ptr(kv_lens), sc, _dtype_code(q), _dtype_code(o), _ptr(workspace), ws_have,
+                                    _stream_handle(q.device)))
+    return dq, dk, dv

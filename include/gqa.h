@@ -184,6 +184,47 @@ int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const v
                         int page_size, int n_pages, int max_pages_per_seq, int d_h, int dtype, void* stream);
 
 /*
+ * gqa_prefill that also writes the row log-sum-exp of the scaled scores,
+ * lse[b][a][i] = log sum_j exp(scale q_i . k_j) over the visible keys (natural
+ * log; -inf for a row with no visible key), fp32 (B, h_q, T).  These per-row
+ * statistics are all the backward pass keeps of the forward ([EffSeq] 在线
+ * softmax: the running maximum m and normalizer l; lse = m + log l).  Arguments
+ * and errors as gqa_prefill, plus INVALID_ARGUMENT for a NULL or misaligned lse.
+ */
+int gqa_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int h_q, int h_kv, int T, int d_h,
+                    int mask, const int32_t* kv_lens, float scale,
+                    int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Bytes of device workspace gqa_prefill_backward needs: one float per query row.
+ * Returns 0 for invalid sizes.
+ */
+size_t gqa_prefill_backward_workspace_bytes(int B, int h_q, int T);
+
+/*
+ * Gradients of prefill attention: dq (B, h_q, T, d_h), dk and dv (B, h_kv, T, d_h),
+ * all fp32, from q, k, v (in_dtype), the forward output o (o_dtype, fp32 or bf16),
+ * its gradient d_o (in_dtype) and the lse gqa_prefill_lse wrote.  Probabilities
+ * are recomputed from lse rather than stored ([EffSeq] 在线 softmax; [AttnVar]
+ * 3.5); the gradients of K/V head g are the sums over its r query heads, formed
+ * inside the library without atomics (results are deterministic).  mask,
+ * kv_lens and scale must be the ones the forward used.  dq, dk, dv are fully
+ * written (zeros for keys no row can see).
+ *   workspace: at least gqa_prefill_backward_workspace_bytes(B, h_q, T) bytes,
+ *     4-byte aligned; contents need no initialisation.
+ * Supported: in_dtype GQA_BF16 with d_h in {64, 128}; otherwise UNSUPPORTED.
+ * Errors: as gqa_prefill for sizes, mask and scale; INVALID_ARGUMENT for a NULL
+ * pointer or misalignment (bf16 tensors and gradients 16-byte aligned);
+ * WORKSPACE_TOO_SMALL.
+ */
+int gqa_prefill_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                         const float* lse, float* dq, float* dk, float* dv,
+                         int B, int h_q, int h_kv, int T, int d_h, int mask, const int32_t* kv_lens,
+                         float scale, int in_dtype, int o_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Rotary position encoding.  Every query head and every stored key head is
  * rotated by its position before scores are formed ([EffSeq] 分组查询注意力:
  * all query heads and each key head actually kept are rotated; [MhaMqaGqa] note

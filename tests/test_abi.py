@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
               "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged",
-              "gqa_rope", "gqa_kv_append_rope"):
+              "gqa_rope", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
+              "gqa_prefill_backward_workspace_bytes"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -150,4 +151,31 @@ def test_rope_validation():
     assert lib.gqa_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 63, 10000.0, 1, None) == \
         ops.GQA_ERR_UNSUPPORTED
     assert lib.gqa_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 64, -1.0, 1, None) == \
+        ops.GQA_ERR_INVALID_ARGUMENT
+
+
+@needs_lib
+def test_backward_validation():
+    lib = ops.load_library()
+    assert lib.gqa_prefill_backward_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 4
+    assert lib.gqa_prefill_backward_workspace_bytes(0, 8, 100) == 0
+    ok = [FAKE] * 9 + [1, 8, 2, 64, 128, 1, None, 0.088, ops.GQA_BF16, ops.GQA_F32, FAKE, 1 << 20, None]
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "h_q", "h_kv", "T", "d", "mask", "lens",
+             "scale", "in", "o_dt", "ws", "wsb", "stream"]
+    def call(**kw):
+        a = list(ok)
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return lib.gqa_prefill_backward(*a)
+    assert call(**{"in": ops.GQA_F32}) == ops.GQA_ERR_UNSUPPORTED
+    assert call(d=96) == ops.GQA_ERR_UNSUPPORTED
+    assert call(h_q=7) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(mask=3) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(lse=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(dq=FAKE + 4) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(wsb=8 * 64 * 4 - 1) == ops.GQA_ERR_WORKSPACE_TOO_SMALL
+    assert call(ws=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_prefill_lse(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == \
+        ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_prefill_lse(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == \
         ops.GQA_ERR_INVALID_ARGUMENT
