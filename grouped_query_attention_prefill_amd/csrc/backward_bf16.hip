@@ -26,6 +26,8 @@
 //   dQ: a workgroup owns 128 query rows (heads x positions of one group, as in
 //     the forward); Q and dO rows stay in registers and 64-key tiles of K and V
 //     stream through LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+#include <type_traits>
+
 #include "internal.h"
 #include "mfma_common.h"
 
@@ -56,6 +58,13 @@ struct BwdParams {
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// dK/dV work item -> (query head, query tile).  Wave-uniform, which the buffer
+// descriptors built from it must be (readfirstlane states it to the compiler).
+__device__ __forceinline__ void dkdv_item(int it, int g, int r, int per_head, int qt0, int& head, int& qt) {
+  head = __builtin_amdgcn_readfirstlane(g * r + it / per_head);
+  qt = __builtin_amdgcn_readfirstlane(qt0 + it % per_head);
+}
 
 // ---------------------------------------------------------------------------
 // delta_i = sum_d dO_id O_id: one wave per row
@@ -100,6 +109,14 @@ bwd_dkdv_kernel(BwdParams p) {
   const int qw = wave >> 1;         // query-tile parity
   const int h = lane >> 5, col = lane & 31;
   const int gtid = tid & 127;       // thread index within the parity pair
+  // parameters the lambdas below use, as scalars (a reference to the whole
+  // parameter block would force it into private memory)
+  const int T = p.T, h_q = p.h_q, r = p.r, causal = p.causal;
+  const float c2 = p.c;
+  const uint16_t* const qp = p.q;
+  const uint16_t* const dop = p.d_o;
+  const float* const lsep = p.lse;
+  const float* const deltap = p.delta;
 
   // heaviest key blocks first: under a causal mask the first keys are seen by every row
   const int n_bg = p.B * p.h_kv;
@@ -142,55 +159,55 @@ bwd_dkdv_kernel(BwdParams p) {
 
   // staging of one item (head, query tile) into region (qw, stage) by the two waves of parity qw
   constexpr int UNITS = kQTile * D / 8 / 128;        // 16-byte chunks per thread per tensor
-  uint4 qreg[UNITS], oreg[UNITS];
-  float lreg = 0.f, dreg = 0.f;
-  auto item_of = [&](int it, int& head, int& qt) {
-    head = g * p.r + it / per_head;
-    qt = qt0 + it % per_head;
-  };
-  auto load_item = [&](int it) {
+  // two register sets: an item's global loads are issued two steps before its
+  // data goes to LDS, so HBM latency hides behind two steps of products
+  uint4 qreg[2][UNITS], oreg[2][UNITS];
+  float lreg[2] = {0.f, 0.f}, dreg[2] = {0.f, 0.f};
+  auto load_item = [&](int it, auto set_tag) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_tag)::value;
     if (it >= n_items) return;
     int head, qt;
-    item_of(it, head, qt);
-    const size_t rbase = ((size_t)(b * p.h_q + head) * p.T) * D;
-    const uint32_t bytes = (uint32_t)p.T * D * 2;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + rbase, bytes);
-    const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.d_o + rbase, bytes);
+    dkdv_item(it, g, r, per_head, qt0, head, qt);
+    const size_t rbase = ((size_t)(b * h_q + head) * T) * D;
+    const uint32_t bytes = (uint32_t)T * D * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp + rbase, bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dop + rbase, bytes);
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = gtid + 128 * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
       const uint32_t off = (uint32_t)(((qt * kQTile + row) * D + c8 * 8) * 2);
-      qreg[i] = load16(qr, off);
-      oreg[i] = load16(dr, off);
+      qreg[set][i] = load16(qr, off);
+      oreg[set][i] = load16(dr, off);
     }
     const int qi = qt * kQTile + (gtid & 31);
-    const size_t li = (size_t)(b * p.h_q + head) * p.T + qi;
-    if (gtid < 32) lreg = qi < p.T ? p.lse[li] : -INFINITY;
-    else if (gtid < 64) dreg = qi < p.T ? p.delta[li] : 0.f;
+    const size_t li = (size_t)(b * h_q + head) * T + qi;
+    // every thread fetches its row's two statistics (threads 0-31 store L, 32-63 delta)
+    lreg[set] = qi < T ? lsep[li] : -INFINITY;
+    dreg[set] = qi < T ? deltap[li] : 0.f;
   };
-  auto region = [&](int par, int stage) { return lds + (par * 2 + stage) * L::REGION; };
-  auto store_item = [&](int it, int stage) {
+  auto store_item = [&](int it, int stage, auto set_tag) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_tag)::value;
     if (it >= n_items) return;
-    unsigned char* rg = region(qw, stage);
+    unsigned char* rg = lds + (qw * 2 + stage) * L::REGION;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = gtid + 128 * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<uint4*>(rg + row * L::TS + c8 * 16) = qreg[i];
-      *reinterpret_cast<uint4*>(rg + L::TILE + row * L::TS + c8 * 16) = oreg[i];
+      *reinterpret_cast<uint4*>(rg + row * L::TS + c8 * 16) = qreg[set][i];
+      *reinterpret_cast<uint4*>(rg + L::TILE + row * L::TS + c8 * 16) = oreg[set][i];
     }
     float* lv = reinterpret_cast<float*>(rg + 2 * L::TILE);
-    if (gtid < 32) lv[gtid] = lreg;
-    else if (gtid < 64) lv[kQTile + (gtid - 32)] = dreg;
+    if (gtid < 32) lv[gtid] = lreg[set];
+    else if (gtid < 64) lv[kQTile + (gtid - 32)] = dreg[set];
   };
 
   // one item on this wave: 32 query rows x 32 keys, 32 products
-  auto compute_item = [&](int it, int stage) {
+  auto compute_item = [&](int it, int stage) __attribute__((always_inline)) {
     int head, qt;
-    item_of(it, head, qt);
+    dkdv_item(it, g, r, per_head, qt0, head, qt);
     (void)head;
-    const unsigned char* rg = region(qw, stage);
+    const unsigned char* rg = lds + (qw * 2 + stage) * L::REGION;
     const unsigned char* qs = rg;
     const unsigned char* os = rg + L::TILE;
     const float* lv = reinterpret_cast<const float*>(rg + 2 * L::TILE);
@@ -204,24 +221,24 @@ bwd_dkdv_kernel(BwdParams p) {
     }
     // rows of element e: query 8 (e / 4) + 4 h + e % 4 of the tile; column: this lane's key
     const int q0 = qt * kQTile;
-    const bool edge = (p.causal && key0 + 31 > q0) || (key0 + 32 > len_b) || (q0 + kQTile > p.T);
+    const bool edge = (causal && key0 + 31 > q0) || (key0 + 32 > len_b) || (q0 + kQTile > T);
     bf16x8 pf[2], dsf[2];
+    float lq[16], dl[16];                 // L and delta of the 16 rows this lane's elements sit in
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const float4 l4 = *reinterpret_cast<const float4*>(lv + 8 * jq + 4 * h);
       const float4 d4 = *reinterpret_cast<const float4*>(lv + kQTile + 8 * jq + 4 * h);
-      const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dq4[4] = {d4.x, d4.y, d4.z, d4.w};
+      lq[4 * jq] = l4.x; lq[4 * jq + 1] = l4.y; lq[4 * jq + 2] = l4.z; lq[4 * jq + 3] = l4.w;
+      dl[4 * jq] = d4.x; dl[4 * jq + 1] = d4.y; dl[4 * jq + 2] = d4.z; dl[4 * jq + 3] = d4.w;
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * jq + i;
-        const int qrow = q0 + 8 * jq + 4 * h + i;
-        bool vis = lq[i] != -INFINITY;
-        if (edge) vis = vis && key < len_b && qrow < p.T && (!p.causal || key <= qrow);
-        const float pr = vis ? fast_exp2(fmaf(sacc[e], p.c, -lq[i] * kLog2e)) : 0.f;
-        sacc[e] = pr;
-        dpacc[e] = pr * (dpacc[e] - dq4[i]);
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int qrow = q0 + 8 * (e >> 2) + 4 * h + (e & 3);
+      bool vis = lq[e] != -INFINITY;
+      if (edge) vis = vis && key < len_b && qrow < T && (!causal || key <= qrow);
+      const float pr = vis ? fast_exp2(fmaf(sacc[e], c2, -lq[e] * kLog2e)) : 0.f;
+      sacc[e] = pr;
+      dpacc[e] = pr * (dpacc[e] - dl[e]);
     }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -244,16 +261,31 @@ bwd_dkdv_kernel(BwdParams p) {
       }
   };
 
-  // ---- pipeline: step s handles items 2s (parity 0) and 2s + 1 (parity 1)
-  load_item(2 * 0 + qw);
-  store_item(qw, 0);
+  // ---- pipeline: step s handles items 2s (parity 0) and 2s + 1 (parity 1).  At step
+  // s, LDS stage s & 1 holds this parity's item of step s, register set (s + 1) & 1
+  // holds the item of step s + 1 (written to the other stage after the products),
+  // and register set s & 1 takes the item of step s + 2.
+  const std::integral_constant<int, 0> set0{};
+  const std::integral_constant<int, 1> set1{};
+  load_item(qw, set0);
+  load_item(2 + qw, set1);
+  store_item(qw, 0, set0);
   lds_barrier();
-  for (int s = 0; s < n_steps; ++s) {
-    const int it = 2 * s + qw;
-    if (s + 1 < n_steps) load_item(it + 2);
-    if (it < n_items) compute_item(it, s & 1);
-    if (s + 1 < n_steps) store_item(it + 2, (s + 1) & 1);
-    lds_barrier();
+  for (int s = 0; s < n_steps; s += 2) {
+    {
+      const int it = 2 * s + qw;
+      if (s + 2 < n_steps) load_item(it + 4, set0);
+      if (it < n_items) compute_item(it, 0);
+      if (s + 1 < n_steps) store_item(it + 2, 1, set1);
+      lds_barrier();
+    }
+    if (s + 1 < n_steps) {
+      const int it = 2 * (s + 1) + qw;
+      if (s + 3 < n_steps) load_item(it + 4, set1);
+      if (it < n_items) compute_item(it, 1);
+      if (s + 2 < n_steps) store_item(it + 2, 0, set0);
+      lds_barrier();
+    }
   }
 
   // ---- add the two parities' partial sums, then write dK = scale dK^T^T and dV
@@ -353,37 +385,44 @@ bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice);
   constexpr int UNITS = kDqTile * D / 8 / kBwdThreads;
-  uint4 kreg[UNITS], vreg[UNITS];
-  auto load_tile = [&](int t) {
+  // two register sets: tile t + 2 is requested while tile t is processed
+  uint4 kreg[2][UNITS], vreg[2][UNITS];
+  auto load_tile = [&](int t, auto set_tag) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_tag)::value;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kBwdThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
       const uint32_t off = (uint32_t)((t * kDqTile + row) * D + c8 * 8) * 2;
-      kreg[i] = load16(krs, off);
-      vreg[i] = load16(vrs, off);
+      kreg[set][i] = load16(krs, off);
+      vreg[set][i] = load16(vrs, off);
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int stage, auto set_tag) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_tag)::value;
     unsigned char* ks_ = lds + stage * L::STAGE;
     unsigned char* vs_ = ks_ + L::K_BYTES;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kBwdThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<uint4*>(ks_ + row * L::KTS + c8 * 16) = kreg[i];
-      *reinterpret_cast<uint4*>(vs_ + row * L::VTS + c8 * 16) = vreg[i];
+      *reinterpret_cast<uint4*>(ks_ + row * L::KTS + c8 * 16) = kreg[set][i];
+      *reinterpret_cast<uint4*>(vs_ + row * L::VTS + c8 * 16) = vreg[set][i];
     }
   };
 
+  const std::integral_constant<int, 0> set0{};
+  const std::integral_constant<int, 1> set1{};
   if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_tile(0, set0);
+    if (n_tiles > 1) load_tile(1, set1);
+    store_tile(0, set0);
   }
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  auto tile_step = [&](const int t, auto set_tag, auto other_tag) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_tag)::value;
+    if (t + 2 < n_tiles) load_tile(t + 2, set_tag);
     lds_barrier();
-    const unsigned char* ks_ = lds + (t & 1) * L::STAGE;
+    const unsigned char* ks_ = lds + set * L::STAGE;
     const unsigned char* vs_ = ks_ + L::K_BYTES;
     const int k0 = t * kDqTile;
     f32x16 sacc[2], dpacc[2];
@@ -424,7 +463,11 @@ bwd_dq_kernel(BwdParams p) {
         const bf16x8 a = load_vt_operand(ks_, L::KTS, kc, db * 32, lane);
         dqacc[db] = mfma32(a, dsf[kc], dqacc[db]);
       }
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+    if (t + 1 < n_tiles) store_tile(set ^ 1, other_tag);
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(t, set0, set1);
+    if (t + 1 < n_tiles) tile_step(t + 1, set1, set0);
   }
 
   if (row_valid) {

@@ -139,11 +139,8 @@ prefill_bf16_kernel(PrefillParams p) {
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY;   // unscaled running maximum of this row
   float l_run = 0.f;         // this lane's share of the normalizer
-  f32x16 s_even[2], s_odd[2];  // S^T of even / odd tiles, two 32-key halves each
-  bf16x8 pf[4];              // P^T of the tile whose PV product comes next
-  float mx_tile = -INFINITY; // masked row maximum of the tile whose exponentials come next
-  float alpha = 1.f;         // rescale factor of O^T before the next PV product
-  bool rescale = false;      // wave-uniform: some row of this wave moved its maximum
+  f32x16 sacc[2];            // S^T of the current tile, two 32-key halves
+  bf16x8 pf[4];              // P^T of the previous tile, four 16-key chunks
 
   // ---- staging: this group's tensor (K or V), global -> registers -> LDS
   const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
@@ -154,63 +151,83 @@ prefill_bf16_kernel(PrefillParams p) {
   const int s_stage = grp == 0 ? L::K_STAGE : L::V_STAGE;
   constexpr int UNITS = kTile * D / 8 / kGroup;             // 16-byte chunks per thread
   uint4 sreg[UNITS];
-  auto load_tile = [&](uint4 (&r)[UNITS], int t) {
+  auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = gtid + kGroup * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      r[i] = load16(srs, (uint32_t)((t * kTile + row) * D + c8 * 8) * 2);
+      sreg[i] = load16(srs, (uint32_t)((t * kTile + row) * D + c8 * 8) * 2);
     }
   };
-  auto store_tile = [&](const uint4 (&r)[UNITS], int t) {
+  auto store_tile = [&](int t) {
     unsigned char* dst = s_base + (t & 1) * s_stage;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = gtid + kGroup * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<uint4*>(dst + row * s_stride + c8 * 16) = r[i];
+      *reinterpret_cast<uint4*>(dst + row * s_stride + c8 * 16) = sreg[i];
     }
   };
 
-  // ---- the two products.  Operand reads run a window ahead of the products that
-  // consume them; a product's accumulator is never needed by the next product.
-  constexpr int NOP = D / 8;     // products per tile and kind
-  constexpr int kWinK = 6;
-  constexpr int kWinV = 4;
-  auto qk_issue = [&](f32x16 (&sd)[2], const int t) {       // S^T of tile t into sd
+  // ---- staging duty of matrix phase t.  Leading group: K tile t + 1 to LDS, K tile
+  // t + 2 requested.  Trailing group: V tile t to LDS, V tile t + 1 requested.
+  // Each write goes to the stage whose previous tile both groups have finished.
+  auto stage_duty = [&](const int t) {
+    const int ts = grp == 0 ? t + 1 : t;
+    if (ts < n_tiles) {
+      store_tile(ts);
+      if (ts + 1 < n_tiles) load_tile(ts + 1);
+    }
+  };
+
+  // ---- matrix phase t: O^T += V^T P^T for tile t - 1 (PV) and S^T = K Q^T for tile t
+  // (QK).  Operand reads run kWin ahead of the products that consume them, in an
+  // order pinned by scheduling barriers, alternating QK and PV products so that no
+  // accumulator is needed again before the product writing it has finished.
+  constexpr int NOP = D / 8;     // operands per product kind and tile
+  constexpr int kWin = 8;
+  constexpr int kStageAt = 8;    // staging duty is issued after this many products
+  auto matrix_phase = [&](const int t, auto qk_tag, auto pv_tag) {
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr int N = (QK ? NOP : 0) + (PV ? NOP : 0);
     const unsigned char* ks_ = lds + (t & 1) * L::K_STAGE;
-    auto kread = [&](int i) {
+    const unsigned char* vs_ = lds + L::V_OFF + ((t - 1) & 1) * L::V_STAGE;
+    auto is_pv = [&](int j) { return QK && PV ? (j & 1) != 0 : PV; };
+    auto idx = [&](int j) { return QK && PV ? j >> 1 : j; };
+    auto read = [&](int j) -> bf16x8 {
+      const int i = idx(j);
+      if (is_pv(j)) return load_vt_operand(vs_, L::VS, i / (D / 32), (i % (D / 32)) * 32, lane);
       return *reinterpret_cast<const bf16x8*>(ks_ + ((i & 1) * 32 + col) * L::KS + ((i >> 1) * 16 + h * 8) * 2);
     };
-    bf16x8 ops[kWinK];
+    bf16x8 ops[kWin];
 #pragma unroll
-    for (int j = 0; j < kWinK; ++j) ops[j] = kread(j);
+    for (int j = 0; j < kWin && j < N; ++j) ops[j] = read(j);
 #pragma unroll
-    for (int j = 0; j < NOP; ++j) {
-      const int kb = j & 1, kd = j >> 1;
-      sd[kb] = mfma32(ops[j % kWinK], qf[kd], kd == 0 ? f32x16{} : sd[kb]);
-      if (j + kWinK < NOP) ops[j % kWinK] = kread(j + kWinK);
+    for (int j = 0; j < N; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = idx(j);
+      if (is_pv(j)) {
+        const int kc = i / (D / 32), db = i % (D / 32);
+        oacc[db] = mfma32(ops[j % kWin], pf[kc], oacc[db]);
+      } else {
+        const int kb = i & 1, kd = i >> 1;
+        sacc[kb] = mfma32(ops[j % kWin], qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
+      }
+      if (j + kWin < N) ops[j % kWin] = read(j + kWin);
+      if (j == kStageAt - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        stage_duty(t);
+      }
     }
-  };
-  auto pv_issue = [&](const int t) {                        // O^T += V^T P^T of tile t
-    const unsigned char* vs_ = lds + L::V_OFF + (t & 1) * L::V_STAGE;
-    auto vread = [&](int i) { return load_vt_operand(vs_, L::VS, i / (D / 32), (i % (D / 32)) * 32, lane); };
-    bf16x8 ops[kWinV];
-#pragma unroll
-    for (int j = 0; j < kWinV; ++j) ops[j] = vread(j);
-#pragma unroll
-    for (int j = 0; j < NOP; ++j) {
-      const int kc = j / (D / 32), db = j % (D / 32);
-      oacc[db] = mfma32(ops[j % kWinV], pf[kc], oacc[db]);
-      if (j + kWinV < NOP) ops[j % kWinV] = vread(j + kWinV);
-    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- softmax pieces.  The running maximum only moves when a tile's maximum
-  // exceeds it by more than 2^kLazyRescale; the decision is branch-free here and
-  // the O^T rescale it may require is applied before the next PV product.
-  auto mask_max = [&](f32x16 (&sd)[2], const int t) {       // mask tile t, its row maximum
+  // ---- vector phase t: online-softmax update from S^T of tile t, P^T for the next
+  // matrix phase; then this group's staging duty: tile t + 1 to LDS, tile t + 2 requested
+  auto vector_phase = [&](const int t) {
     const int k0 = t * kTile;
+    // mask only where some key of the tile may be invisible to some row
     const bool need_mask = (p.causal && k0 + kTile - 1 > min_pos) || (k0 + kTile > len_b);
     if (need_mask) {
 #pragma unroll
@@ -219,140 +236,70 @@ prefill_bf16_kernel(PrefillParams p) {
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
           const bool vis = key < len_b && (!p.causal || key <= pos);
-          sd[kb][e] = vis ? sd[kb][e] : -INFINITY;
+          sacc[kb][e] = vis ? sacc[kb][e] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sd[kb][e]);
-    mx_tile = pair_max(mx);
-  };
-  auto exps_pack = [&](f32x16 (&sd)[2]) {                   // P of the tile with maximum mx_tile
-    const bool grow = (mx_tile - m_run) * p.c > kLazyRescale;   // false for -inf - (-inf)
-    alpha = grow ? fast_exp2((m_run - mx_tile) * p.c) : 1.f;    // 0 on the first visible tile
-    rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
-    m_run = grow ? mx_tile : m_run;
-    l_run *= alpha;
-    const float mc = (m_run == -INFINITY ? 0.f : m_run) * p.c;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sd[kb][e] = fast_exp2(fmaf(sd[kb][e], p.c, -mc));
-    // P^T fragments: chunk kc of the tile = elements 8*(kc&1) .. +7 of half kc>>1
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const f32x16& sv = sd[kc >> 1];
-      const int e0 = 8 * (kc & 1);
-      pf[kc] = pack_bf16x8(sv[e0], sv[e0 + 1], sv[e0 + 2], sv[e0 + 3], sv[e0 + 4], sv[e0 + 5], sv[e0 + 6], sv[e0 + 7]);
-    }
-  };
-  auto psum_add = [&](const f32x16 (&sd)[2]) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      a0 += sd[0][e]; a1 += sd[0][e + 1]; a2 += sd[1][e]; a3 += sd[1][e + 1];
-    }
-    l_run += (a0 + a1) + (a2 + a3);
-  };
-
-  // ---- phases.  A(t): S^T of tile t + 1 on the matrix core while the vector unit
-  // computes P of tile t.  B(t): O^T += V^T P^T of tile t beside the row sums of P;
-  // then this group's staging duty and the maximum of tile t + 1.  Every phase
-  // issues its products and its vector work as one interleaved stream, so one wave
-  // keeps both units busy; the two groups run one phase apart.
-  auto phase_a = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const int t, auto next_tag) {
-    constexpr bool NEXT = decltype(next_tag)::value;
-    if constexpr (NEXT) qk_issue(sn, t + 1);
-    exps_pack(sc);
-    if constexpr (NEXT) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kWinK, 0);   // first operand reads
-#pragma unroll
-      for (int j = 0; j < NOP; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one product
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one operand read
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);     // vector work
-      }
-    }
-  };
-  auto phase_b = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], const int t, auto next_tag) {
-    constexpr bool NEXT = decltype(next_tag)::value;
-    if (rescale) {
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = pair_max(mx);
+    // move the running maximum only when it grew by more than 2^kLazyRescale
+    const bool grow = (mx - m_run) * p.c > kLazyRescale;     // false for -inf - (-inf)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2((m_run - mx) * p.c) : 1.f;   // 0 on the first visible tile
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m_run = grow ? mx : m_run;
     }
-    pv_issue(t);
-    psum_add(sc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWinV, 0);
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * p.c;
+    float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < NOP; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(fmaf(sacc[kb][e], p.c, -mc));
+        sacc[kb][e] = pe;
+        psum += pe;
+      }
+    l_run += psum;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const f32x16& sv = sacc[kc >> 1];
+      const int e0 = 8 * (kc & 1);
+      pf[kc] = pack_bf16x8(sv[e0], sv[e0 + 1], sv[e0 + 2], sv[e0 + 3], sv[e0 + 4], sv[e0 + 5], sv[e0 + 6], sv[e0 + 7]);
     }
-    // staging: the leading group writes K tile t + 2 and requests t + 3, the
-    // trailing group writes V tile t + 1 and requests t + 2
-    const int ts = grp == 0 ? t + 2 : t + 1;
-    if (ts < n_tiles) {
-      store_tile(sreg, ts);
-      if (ts + 1 < n_tiles) load_tile(sreg, ts + 1);
-    }
-    if constexpr (NEXT) mask_max(sn, t + 1);
   };
 
-  // ---- pipeline.  Global phase k: the leading group runs its phase k, the trailing
-  // group its phase k - 1; every wave passes the same barriers.  K tile j is read in
-  // phases 2j - 1 (lead) and 2j (trail) (tile 0: phases 0 and 1), V tile t in phases
-  // 2t + 2 and 2t + 3; K tile t + 2 is written in phase 2t + 2 and V tile t + 1 in
-  // phase 2t + 3, each into the stage whose previous tile both groups are past.
+  // ---- pipeline.  Phase k of the leading group runs beside phase k - 1 of the
+  // trailing one; both issue the same number of barriers.  K tile t is read in
+  // matrix phase t, V tile t in matrix phase t + 1; a stage is rewritten only
+  // after both groups are past its last reader.
   if (n_tiles > 0) {
     const auto yes = std::integral_constant<bool, true>{};
     const auto no = std::integral_constant<bool, false>{};
-    load_tile(sreg, 0);
+    load_tile(0);
     if (grp == 0) {
-      uint4 r1[UNITS];
-      if (n_tiles > 1) load_tile(r1, 1);
-      store_tile(sreg, 0);
-      if (n_tiles > 1) {
-        store_tile(r1, 1);
-        if (n_tiles > 2) load_tile(sreg, 2);
-      }
-    } else {
-      store_tile(sreg, 0);
-      if (n_tiles > 1) load_tile(sreg, 1);
+      store_tile(0);
+      if (n_tiles > 1) load_tile(1);
     }
     lds_barrier();
     if (grp == 1) lds_barrier();   // the trailing group starts one phase late
-    qk_issue(s_even, 0);
-    mask_max(s_even, 0);
+    matrix_phase(0, yes, no);
     lds_barrier();
-    int t = 0;
-    for (; t + 2 < n_tiles; t += 2) {
-      phase_a(s_even, s_odd, t, yes);
+    vector_phase(0);
+    lds_barrier();
+    for (int t = 1; t < n_tiles; ++t) {
+      matrix_phase(t, yes, yes);
       lds_barrier();
-      phase_b(s_even, s_odd, t, yes);
-      lds_barrier();
-      phase_a(s_odd, s_even, t + 1, yes);
-      lds_barrier();
-      phase_b(s_odd, s_even, t + 1, yes);
+      vector_phase(t);
       lds_barrier();
     }
-    if (t + 1 < n_tiles) {         // two tiles left: t even, t + 1 last
-      phase_a(s_even, s_odd, t, yes);
-      lds_barrier();
-      phase_b(s_even, s_odd, t, yes);
-      lds_barrier();
-      phase_a(s_odd, s_even, t + 1, no);
-      lds_barrier();
-      phase_b(s_odd, s_even, t + 1, no);
-    } else {                       // one tile left: t even
-      phase_a(s_even, s_odd, t, no);
-      lds_barrier();
-      phase_b(s_even, s_odd, t, no);
-    }
+    matrix_phase(n_tiles, no, yes);
     if (grp == 0) lds_barrier();   // pairs with the trailing group's last barrier
   }
 
@@ -361,7 +308,9 @@ prefill_bf16_kernel(PrefillParams p) {
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (row_valid && p.lse && h == 0) {
     // l_tot sums exp(scale (s - m)) with m the unscaled running maximum
-    p.lse[(size_t)(b * p.h_q + head) * p.S_q + qi] = l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+    constexpr float kLn2 = 0.6931471805599453f;
+    p.lse[(size_t)(b * p.h_q + head) * p.S_q + qi] =
+        l_tot > 0.f ? fmaf(__builtin_amdgcn_logf(l_tot), kLn2, m_run * p.scale) : -INFINITY;
   }
   if (row_valid) {
     const size_t obase = ((size_t)(b * p.h_q + head) * p.S_q + qi) * D;
