@@ -25,7 +25,8 @@
 //     add their partial sums at the end.
 //   dQ: a workgroup owns 128 query rows (heads x positions of one group, as in
 //     the forward); Q and dO rows stay in registers and 64-key tiles of K and V
-//     stream through LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+//     stream through LDS, each worked in two 32-key halves (S^T = K Q^T,
+//     dP^T = V dO^T, dQ^T += K^T dS^T) so that two workgroups fit a CU.
 #include <type_traits>
 
 #include "internal.h"
@@ -331,7 +332,7 @@ struct DqLds {
 };
 
 template <int D>
-__global__ void __launch_bounds__(kBwdThreads, 1)
+__global__ void __launch_bounds__(kBwdThreads, 2)
 bwd_dq_kernel(BwdParams p) {
   using L = DqLds<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -385,89 +386,75 @@ bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice);
   constexpr int UNITS = kDqTile * D / 8 / kBwdThreads;
-  // two register sets: tile t + 2 is requested while tile t is processed
-  uint4 kreg[2][UNITS], vreg[2][UNITS];
-  auto load_tile = [&](int t, auto set_tag) __attribute__((always_inline)) {
-    constexpr int set = decltype(set_tag)::value;
+  uint4 kreg[UNITS], vreg[UNITS];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kBwdThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
       const uint32_t off = (uint32_t)((t * kDqTile + row) * D + c8 * 8) * 2;
-      kreg[set][i] = load16(krs, off);
-      vreg[set][i] = load16(vrs, off);
+      kreg[i] = load16(krs, off);
+      vreg[i] = load16(vrs, off);
     }
   };
-  auto store_tile = [&](int stage, auto set_tag) __attribute__((always_inline)) {
-    constexpr int set = decltype(set_tag)::value;
+  auto store_tile = [&](int stage) __attribute__((always_inline)) {
     unsigned char* ks_ = lds + stage * L::STAGE;
     unsigned char* vs_ = ks_ + L::K_BYTES;
 #pragma unroll
     for (int i = 0; i < UNITS; ++i) {
       const int u = tid + kBwdThreads * i;
       const int row = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<uint4*>(ks_ + row * L::KTS + c8 * 16) = kreg[set][i];
-      *reinterpret_cast<uint4*>(vs_ + row * L::VTS + c8 * 16) = vreg[set][i];
+      *reinterpret_cast<uint4*>(ks_ + row * L::KTS + c8 * 16) = kreg[i];
+      *reinterpret_cast<uint4*>(vs_ + row * L::VTS + c8 * 16) = vreg[i];
     }
   };
-
-  const std::integral_constant<int, 0> set0{};
-  const std::integral_constant<int, 1> set1{};
   if (n_tiles > 0) {
-    load_tile(0, set0);
-    if (n_tiles > 1) load_tile(1, set1);
-    store_tile(0, set0);
+    load_tile(0);
+    store_tile(0);
   }
-  auto tile_step = [&](const int t, auto set_tag, auto other_tag) __attribute__((always_inline)) {
-    constexpr int set = decltype(set_tag)::value;
-    if (t + 2 < n_tiles) load_tile(t + 2, set_tag);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int set = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
     lds_barrier();
     const unsigned char* ks_ = lds + set * L::STAGE;
     const unsigned char* vs_ = ks_ + L::K_BYTES;
     const int k0 = t * kDqTile;
-    f32x16 sacc[2], dpacc[2];
+    const bool edge = (p.causal && k0 + kDqTile - 1 > first_q) || (k0 + kDqTile > len_b);
+    // the tile in two 32-key halves, each: S^T, dP^T, dS^T, then its two 16-key chunks of dQ^T
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc, dpacc;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kd = 0; kd < D / 16; ++kd) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks_ + (kb * 32 + col) * L::KTS + (kd * 16 + h * 8) * 2);
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(vs_ + (kb * 32 + col) * L::VTS + (kd * 16 + h * 8) * 2);
-        sacc[kb] = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
-        dpacc[kb] = mfma32(v, of[kd], kd == 0 ? f32x16{} : dpacc[kb]);
+        sacc = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc);
+        dpacc = mfma32(v, of[kd], kd == 0 ? f32x16{} : dpacc);
       }
-    // rows of element e: key k0 + 32 kb + 8 (e / 4) + 4 h + e % 4; column: this lane's query
-    const bool edge = (p.causal && k0 + kDqTile - 1 > first_q) || (k0 + kDqTile > len_b);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
         bool vis = lrow != -INFINITY;
         if (edge) vis = vis && kk < len_b && (!p.causal || kk <= qi);
-        const float pr = vis ? fast_exp2(fmaf(sacc[kb][e], p.c, -lc)) : 0.f;
-        dpacc[kb][e] = pr * (dpacc[kb][e] - drow);
+        const float pr = vis ? fast_exp2(fmaf(sacc[e], p.c, -lc)) : 0.f;
+        dpacc[e] = pr * (dpacc[e] - drow);
       }
-    bf16x8 dsf[4];
+      bf16x8 dsf[2];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const f32x16& sv = dpacc[kc >> 1];
-      const int e0 = 8 * (kc & 1);
-      dsf[kc] = pack_bf16x8(sv[e0], sv[e0 + 1], sv[e0 + 2], sv[e0 + 3], sv[e0 + 4], sv[e0 + 5], sv[e0 + 6],
-                            sv[e0 + 7]);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int e0 = 8 * c2;
+        dsf[c2] = pack_bf16x8(dpacc[e0], dpacc[e0 + 1], dpacc[e0 + 2], dpacc[e0 + 3], dpacc[e0 + 4], dpacc[e0 + 5],
+                              dpacc[e0 + 6], dpacc[e0 + 7]);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 a = load_vt_operand(ks_, L::KTS, 2 * kb + c2, db * 32, lane);
+          dqacc[db] = mfma32(a, dsf[c2], dqacc[db]);
+        }
     }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = load_vt_operand(ks_, L::KTS, kc, db * 32, lane);
-        dqacc[db] = mfma32(a, dsf[kc], dqacc[db]);
-      }
-    if (t + 1 < n_tiles) store_tile(set ^ 1, other_tag);
-  };
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile_step(t, set0, set1);
-    if (t + 1 < n_tiles) tile_step(t + 1, set1, set0);
+    if (t + 1 < n_tiles) store_tile(set ^ 1);
   }
 
   if (row_valid) {
