@@ -8,7 +8,8 @@ Recipe (the same for every workload):
   * numpy PCG64 streams keyed by ``SeedSequence(seed, spawn_key=(tensor, row))``:
     one independent stream per tensor and per batch row, so rows can be drawn
     in parallel threads and any row can be regenerated on its own;
-    tensor ids: Q 0, K 1, V 2, appended K 3, appended V 4, lengths 5 (one stream);
+    tensor ids: Q 0, K 1, V 2, appended K 3, appended V 4, lengths 5 (one stream),
+    output gradient dO 6;
   * values are ``standard_normal(dtype=float32)``, i.e. N(0, 1);
   * bf16 tensors are those float32 draws rounded to bf16, round-to-nearest-even;
     both sides see exactly those bf16 values (the oracle widens them to float64
@@ -35,7 +36,7 @@ SEED_BASE = 1949
 BF16_QNAN = np.uint16(0x7FC0)
 
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "k_new": 3, "v_new": 4, "lengths": 5}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "k_new": 3, "v_new": 4, "lengths": 5, "d_out": 6}
 
 
 def rng_for(seed: int, tensor: int = 5, row: int = 0) -> np.random.Generator:

@@ -44,7 +44,7 @@ def _run(B, h_q, h_kv, T, d, causal, seed, kv_lens=None, out_dtype="f32"):
     import torch
 
     x = inputs.make_prefill(B, h_q, h_kv, d, T, "bf16", seed)
-    d_out = inputs.normal(seed, "k_new", (B, h_q, T, d), "bf16")      # dO drawn from its own stream
+    d_out = inputs.normal(seed, "d_out", (B, h_q, T, d), "bf16")
     q, k, v, do = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(d_out, "bf16")
     lens = None if kv_lens is None else ints_dev(kv_lens)
     od = torch.float32 if out_dtype == "f32" else torch.bfloat16
@@ -122,7 +122,7 @@ def test_backward_prefill_workload_sampled():
     w = inputs.WORKLOADS["prefill_causal_bf16_T4096"]
     print(f"case {w.name} backward", flush=True)
     x = inputs.make_workload(w)
-    d_out = inputs.normal(w.seed, "k_new", (w.B, w.h_q, w.T, w.d_h), "bf16")
+    d_out = inputs.normal(w.seed, "d_out", (w.B, w.h_q, w.T, w.d_h), "bf16")
     q, k, v, do = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(d_out, "bf16")
     o, lse = ops.gqa_prefill_lse(q, k, v)
     dq, dk, dv = ops.gqa_prefill_backward(q, k, v, o, do, lse)
