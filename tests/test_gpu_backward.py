@@ -31,7 +31,8 @@ def _check_grad(got, want, what):
     nrm = np.linalg.norm(want)
     err = got - want
     if nrm == 0.0:
-        assert np.max(np.abs(got)) == 0.0, f"{what}: expected zeros"
+        # exact answer 0 (a one-key row: dP - delta cancels); fp32 rounding of O(1) terms remains
+        assert np.max(np.abs(got)) <= 1e-5, f"{what}: expected zeros, got {np.max(np.abs(got)):.3g}"
         return
     rel = np.linalg.norm(err) / nrm
     mx = np.max(np.abs(err)) / np.max(np.abs(want))
