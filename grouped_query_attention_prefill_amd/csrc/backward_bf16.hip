@@ -166,11 +166,14 @@ bwd_dkdv_kernel(BwdParams p) {
   float lreg[2] = {0.f, 0.f}, dreg[2] = {0.f, 0.f};
   auto load_item = [&](int it, auto set_tag) __attribute__((always_inline)) {
     constexpr int set = decltype(set_tag)::value;
-    if (it >= n_items) return;
+    // past the last item the loads still issue, through empty descriptors that
+    // return zeros: every step then issues the same loads, which lets the compiler
+    // count exactly which of them a later wait needs
+    const bool valid = it < n_items;
     int head, qt;
-    dkdv_item(it, g, r, per_head, qt0, head, qt);
+    dkdv_item(valid ? it : 0, g, r, per_head, qt0, head, qt);
     const size_t rbase = ((size_t)(b * h_q + head) * T) * D;
-    const uint32_t bytes = (uint32_t)T * D * 2;
+    const uint32_t bytes = valid ? (uint32_t)T * D * 2 : 0u;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp + rbase, bytes);
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(dop + rbase, bytes);
 #pragma unroll
@@ -182,10 +185,14 @@ bwd_dkdv_kernel(BwdParams p) {
       oreg[set][i] = load16(dr, off);
     }
     const int qi = qt * kQTile + (gtid & 31);
-    const size_t li = (size_t)(b * h_q + head) * T + qi;
-    // every thread fetches its row's two statistics (threads 0-31 store L, 32-63 delta)
-    lreg[set] = qi < T ? lsep[li] : -INFINITY;
-    dreg[set] = qi < T ? deltap[li] : 0.f;
+    const size_t li = (size_t)(b * h_q + head) * T;
+    // every thread fetches its row's two statistics (threads 0-31 store L, 32-63
+    // delta); rows at or past T read 0, and the edge mask drops them
+    const uint32_t sbytes = valid ? (uint32_t)T * 4 : 0u;
+    lreg[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(lsep + li, sbytes),
+                                                                             qi * 4, 0, 0));
+    dreg[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(deltap + li, sbytes),
+                                                                             qi * 4, 0, 0));
   };
   auto store_item = [&](int it, int stage, auto set_tag) __attribute__((always_inline)) {
     constexpr int set = decltype(set_tag)::value;
@@ -232,15 +239,25 @@ bwd_dkdv_kernel(BwdParams p) {
       lq[4 * jq] = l4.x; lq[4 * jq + 1] = l4.y; lq[4 * jq + 2] = l4.z; lq[4 * jq + 3] = l4.w;
       dl[4 * jq] = d4.x; dl[4 * jq + 1] = d4.y; dl[4 * jq + 2] = d4.z; dl[4 * jq + 3] = d4.w;
     }
+    // P = exp2(c s - L log2 e); masked entries take exp2(-inf) = 0.  Inside the
+    // key range, below the diagonal and above T every row sees key 0, so L is
+    // finite and no mask is needed off the edge tiles.
+    auto probs = [&](auto masked_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int qrow = q0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      bool vis = lq[e] != -INFINITY;
-      if (edge) vis = vis && key < len_b && qrow < T && (!causal || key <= qrow);
-      const float pr = vis ? fast_exp2(fmaf(sacc[e], c2, -lq[e] * kLog2e)) : 0.f;
-      sacc[e] = pr;
-      dpacc[e] = pr * (dpacc[e] - dl[e]);
-    }
+      for (int e = 0; e < 16; ++e) {
+        float arg = fmaf(sacc[e], c2, -lq[e] * kLog2e);
+        if constexpr (decltype(masked_tag)::value) {
+          const int qrow = q0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          const bool vis = (lq[e] != -INFINITY) & (key < len_b) & (qrow < T) & (!causal | (key <= qrow));
+          arg = vis ? arg : -INFINITY;
+        }
+        const float pr = fast_exp2(arg);
+        sacc[e] = pr;
+        dpacc[e] = pr * (dpacc[e] - dl[e]);
+      }
+    };
+    if (edge) probs(std::true_type{});
+    else probs(std::false_type{});
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const int e0 = 8 * kc;
@@ -272,19 +289,27 @@ bwd_dkdv_kernel(BwdParams p) {
   load_item(2 + qw, set1);
   store_item(qw, 0, set0);
   lds_barrier();
+  // The K and V fragments are in registers before the loop starts (the staging
+  // above waited for them); the empty asm makes that explicit to the compiler,
+  // which otherwise carries their pending loads into the loop and waits there
+  // for every load in flight, prefetches included.
+#pragma unroll
+  for (int kd = 0; kd < D / 16; ++kd) asm volatile("" : "+v"(kf[kd]), "+v"(vf[kd]));
+  // steps run in pairs (an odd count ends with an empty step) so that both
+  // register sets are named at compile time
   for (int s = 0; s < n_steps; s += 2) {
     {
       const int it = 2 * s + qw;
-      if (s + 2 < n_steps) load_item(it + 4, set0);
+      load_item(it + 4, set0);
       if (it < n_items) compute_item(it, 0);
-      if (s + 1 < n_steps) store_item(it + 2, 1, set1);
+      store_item(it + 2, 1, set1);
       lds_barrier();
     }
-    if (s + 1 < n_steps) {
+    {
       const int it = 2 * (s + 1) + qw;
-      if (s + 3 < n_steps) load_item(it + 4, set1);
+      load_item(it + 4, set1);
       if (it < n_items) compute_item(it, 1);
-      if (s + 2 < n_steps) store_item(it + 2, 0, set0);
+      store_item(it + 2, 0, set0);
       lds_barrier();
     }
   }
