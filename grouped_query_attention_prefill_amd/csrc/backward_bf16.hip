@@ -393,7 +393,11 @@ bwd_dq_kernel(BwdParams p) {
   }
   const float lrow = row_valid ? p.lse[rrow] : -INFINITY;
   const float drow = row_valid ? p.delta[rrow] : 0.f;
-  const float lc = lrow * kLog2e;
+  // a row outside the sequence, or one that sees no key, has L = -inf; its exp2
+  // arguments are then made -inf so that all of its P are 0
+  const float lc = lrow != -INFINITY ? lrow * kLog2e : INFINITY;
+  const int causal = p.causal;
+  const float c2 = p.c;
 
   f32x16 dqacc[D / 32];
 #pragma unroll
@@ -456,14 +460,21 @@ bwd_dq_kernel(BwdParams p) {
         sacc = mfma32(a, qf[kd], kd == 0 ? f32x16{} : sacc);
         dpacc = mfma32(v, of[kd], kd == 0 ? f32x16{} : dpacc);
       }
+      // masked entries take exp2(-inf) = 0; off the edge tiles every key is visible
+      auto grads = [&](auto masked_tag) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        bool vis = lrow != -INFINITY;
-        if (edge) vis = vis && kk < len_b && (!p.causal || kk <= qi);
-        const float pr = vis ? fast_exp2(fmaf(sacc[e], p.c, -lc)) : 0.f;
-        dpacc[e] = pr * (dpacc[e] - drow);
-      }
+        for (int e = 0; e < 16; ++e) {
+          float arg = fmaf(sacc[e], c2, -lc);
+          if constexpr (decltype(masked_tag)::value) {
+            const int kk = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const bool vis = (kk < len_b) & (!causal | (kk <= qi));
+            arg = vis ? arg : -INFINITY;
+          }
+          dpacc[e] = fast_exp2(arg) * (dpacc[e] - drow);
+        }
+      };
+      if (edge) grads(std::true_type{});
+      else grads(std::false_type{});
       bf16x8 dsf[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
