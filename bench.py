@@ -1,6 +1,6 @@
 """Benchmark of the grouped-query attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--no-cpu-baseline] [--no-sweep]
 
 Headline step: one causal bf16 prefill of the workload B=1, h_q=32, h_kv=8,
 d_h=128, T=4096 (fp32 output), whose throughput is reported as TFLOP/s of
@@ -31,6 +31,12 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
 FLUSH_BYTES = 512 << 20        # larger than the 256 MB Infinity Cache
 METRIC = "GQA decode HBM GB/s (% peak) + causal prefill TFLOP/s (% MFMA peak), 1 GPU"
+# Untimed back-to-back launches before each timed region.  Coming out of idle (even
+# 0.2 s of it) the GPU needs ~40 ms of sustained load before its clocks settle: the
+# prefill kernel takes 0.16-0.17 ms per launch for the first ~200 launches and
+# 0.138 ms after.  Every leg starts after seconds of host-side input generation, so
+# each one settles first and the timed steps measure the sustained rate.
+SETTLE_S = 0.3
 
 # decode workloads timed besides the headline ones: (workload, page size or 0 for a contiguous cache)
 SWEEP = [("decode_mha_B8_T32000", 0), ("decode_gqa_B8_T32000", 0), ("decode_mqa_B8_T32000", 0),
@@ -68,6 +74,22 @@ def measured_traffic(kernel: str, workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
+def settle(fn, seconds: float):
+    """Call fn back to back, untimed, for at least `seconds` of wall time."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while seconds > 0:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        n += 8
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return n
+
+
 def time_calls(fn, steps: int, warmup: int, flush=None):
     """Run fn warmup+steps times; HIP events around every timed call on the current stream.
 
@@ -77,6 +99,7 @@ def time_calls(fn, steps: int, warmup: int, flush=None):
 
     for _ in range(warmup):
         fn()
+    settle((lambda: (flush(), fn())) if flush is not None else fn, SETTLE_S)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -100,6 +123,7 @@ def time_region(fn, steps: int, warmup: int):
 
     for _ in range(warmup):
         fn()
+    settle(fn, SETTLE_S)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -376,10 +400,13 @@ def bench_copy(steps, warmup):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed back-to-back launches before each timed region (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy", "rope", "backward"],
@@ -397,6 +424,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     steps, warmup = max(1, args.steps), max(0, args.warmup)
+    SETTLE_S = max(0.0, args.settle)
 
     if args.only == "copy":
         print(json.dumps(bench_copy(steps, warmup)), flush=True)
@@ -439,6 +467,7 @@ def main():
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(pre["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

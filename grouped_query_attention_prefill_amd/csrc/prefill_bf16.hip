@@ -29,7 +29,9 @@
 // the two groups in step.  The groups also split the staging: the leading group
 // streams K tiles and the trailing group V tiles, each through registers into
 // a double-buffered LDS stage, written in the middle of the group's matrix phase
-// (global loads are requested two phases before their data is written).
+// (global loads are requested two phases before their data is written).  A
+// matrix phase opens with a few QK products whose K operands were read before
+// its barrier.
 //
 // Layouts in LDS, both filled by 16-byte buffer loads that return zeros past the
 // last visible key (no per-load branches):
@@ -187,22 +189,52 @@ prefill_bf16_kernel(PrefillParams p) {
   constexpr int NOP = D / 8;     // operands per product kind and tile
   constexpr int kWin = 8;
   constexpr int kStageAt = 8;    // staging duty is issued after this many products
-  auto matrix_phase = [&](const int t, auto qk_tag, auto pv_tag) {
+  // The first NPRE QK operands of matrix phase t are read at the end of the vector
+  // phase before it, ahead of the barrier, so the phase opens with products whose
+  // operands are already in registers while its V reads are still in flight.  K
+  // tile t was written during the leading group's matrix phase t - 1 and a barrier
+  // has passed since; its stage is next written with K tile t + 2, in matrix phase
+  // t + 1 of the leading group, after both groups' matrix phase t.
+  constexpr int NPRE = 4;
+  bf16x8 ops[kWin];
+  auto pre_read = [&](const int t) {
+    const unsigned char* ks_ = lds + (t & 1) * L::K_STAGE;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i)
+      ops[i] = *reinterpret_cast<const bf16x8*>(ks_ + ((i & 1) * 32 + col) * L::KS + ((i >> 1) * 16 + h * 8) * 2);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto matrix_phase = [&](const int t, auto qk_tag, auto pv_tag, auto pre_tag) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool PRE = decltype(pre_tag)::value;
     constexpr int N = (QK ? NOP : 0) + (PV ? NOP : 0);
     const unsigned char* ks_ = lds + (t & 1) * L::K_STAGE;
     const unsigned char* vs_ = lds + L::V_OFF + ((t - 1) & 1) * L::V_STAGE;
-    auto is_pv = [&](int j) { return QK && PV ? (j & 1) != 0 : PV; };
-    auto idx = [&](int j) { return QK && PV ? j >> 1 : j; };
+    // order: NPRE QK products first (their operands were read before the barrier),
+    // then PV and QK alternating, then the remaining PV products
+    auto is_pv = [&](int j) -> bool {
+      if (!(QK && PV)) return PV;
+      if (j < NPRE) return false;
+      const int m = j - NPRE;
+      if (m < 2 * (NOP - NPRE)) return (m & 1) == 0;
+      return true;
+    };
+    auto idx = [&](int j) -> int {
+      if (!(QK && PV)) return j;
+      if (j < NPRE) return j;
+      const int m = j - NPRE;
+      if (m < 2 * (NOP - NPRE)) return (m & 1) == 0 ? m / 2 : NPRE + m / 2;
+      return (NOP - NPRE) + (m - 2 * (NOP - NPRE));
+    };
     auto read = [&](int j) -> bf16x8 {
       const int i = idx(j);
       if (is_pv(j)) return load_vt_operand(vs_, L::VS, i / (D / 32), (i % (D / 32)) * 32, lane);
       return *reinterpret_cast<const bf16x8*>(ks_ + ((i & 1) * 32 + col) * L::KS + ((i >> 1) * 16 + h * 8) * 2);
     };
-    bf16x8 ops[kWin];
 #pragma unroll
-    for (int j = 0; j < kWin && j < N; ++j) ops[j] = read(j);
+    for (int j = PRE ? NPRE : 0; j < kWin && j < N; ++j) ops[j] = read(j);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       __builtin_amdgcn_sched_barrier(0);
@@ -289,17 +321,19 @@ prefill_bf16_kernel(PrefillParams p) {
     }
     lds_barrier();
     if (grp == 1) lds_barrier();   // the trailing group starts one phase late
-    matrix_phase(0, yes, no);
+    matrix_phase(0, yes, no, no);
     lds_barrier();
     vector_phase(0);
+    if (1 < n_tiles) pre_read(1);
     lds_barrier();
     for (int t = 1; t < n_tiles; ++t) {
-      matrix_phase(t, yes, yes);
+      matrix_phase(t, yes, yes, yes);
       lds_barrier();
       vector_phase(t);
+      if (t + 1 < n_tiles) pre_read(t + 1);
       lds_barrier();
     }
-    matrix_phase(n_tiles, no, yes);
+    matrix_phase(n_tiles, no, yes, no);
     if (grp == 0) lds_barrier();   // pairs with the trailing group's last barrier
   }
 
