@@ -42,6 +42,7 @@ DECODE_CASES = [
     ("bf16", 2, 4, 4, 2100, 64, [2100, 1300]),        # MHA, d_h 64
     ("bf16", 2, 12, 4, 257, 128, [257, 129]),         # r=3, lengths straddling tiles
     ("bf16", 4, 32, 8, 9000, 128, [9000, 8192, 4097, 33]),
+    ("bf16", 1, 16, 1, 9000, 128, [9000]),            # r=16 on the 16x16 kernel, 36 splits
     ("f32", 3, 8, 2, 300, 40, [300, 151, 1]),
     ("f32", 1, 32, 1, 100, 128, [100]),
 ]
@@ -93,6 +94,33 @@ def test_decode_equals_last_prefill_row_bf16():
 def test_decode_deterministic():
     x = inputs.make_decode(2, 32, 8, 128, 4000, "bf16", 11400)
     assert np.array_equal(_decode(x, "bf16"), _decode(x, "bf16"))
+
+
+def test_decode_reused_workspace():
+    """One workspace reused by many calls, of two shapes in turn: the partial states of
+    one call never leak into another (results bit-identical to the first call of each
+    shape, which matches the oracle)."""
+    import torch
+
+    shapes = [(8, 32, 8, 8000, [8000, 7000, 6000, 5000, 4000, 3000, 2000, 1000]), (3, 16, 4, 5000, [5000, 64, 1])]
+    ws_bytes = max(ops.gqa_decode_workspace_bytes(B, hq, hkv, T, 128, torch.bfloat16) for B, hq, hkv, T, _ in shapes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    runs = []
+    for i, (B, hq, hkv, T, lens) in enumerate(shapes):
+        x = inputs.make_decode(B, hq, hkv, 128, T, "bf16", 11500 + i, seq_lens=lens, poison=True)
+        dev = (to_dev(x["q"], "bf16"), to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16"), ints_dev(x["seq_lens"]))
+        runs.append((x, dev))
+    first = [None, None]
+    for it in range(40):
+        for i, (x, (q, k, v, sl)) in enumerate(runs):
+            o = ops.gqa_decode(q, k, v, sl, workspace=ws)
+            torch.cuda.synchronize()
+            got = to_host64(o)
+            if first[i] is None:
+                first[i] = got
+                check_parity(got, _oracle_decode(x, "bf16"), mode="bf16", what=f"reused workspace shape {i}")
+            else:
+                assert np.array_equal(got, first[i]), (it, i)
 
 
 # ---------------------------------------------------------------- kv_append
