@@ -29,6 +29,7 @@ constexpr int kThreads = 256;
 constexpr int kTile = 128;          // keys per workgroup tile (32 per wave)
 constexpr int kTargetWG = 512;      // workgroups the split heuristic aims for (2 resident per CU)
 constexpr int kMinChunk = 256;      // smallest history slice per workgroup
+constexpr int kManySplits = 8;      // above this many splits the batched merge kernel runs
 
 struct DecodeParams {
   const uint16_t* q;
@@ -613,6 +614,72 @@ decode_combine_kernel(DecodeParams p) {
   }
 }
 
+// The same merge for many splits (more than kManySplits): thread (split lane j,
+// unit q) folds splits j, j + NJ, j + 2 NJ, ... for d = 4q .. 4q + 3, with the
+// states of eight of its splits requested at once instead of one split after
+// another; the NJ states of a unit are then folded in LDS in split-lane order.
+template <int D, bool OUT_BF16>
+__global__ void __launch_bounds__(256)
+decode_combine_many_kernel(DecodeParams p) {
+  constexpr int Q = D / 4;             // 4-wide units of d
+  constexpr int NJ = 256 / Q;          // split lanes
+  __shared__ float4 st_u[NJ][Q];
+  __shared__ float2 st_ml[NJ][Q];
+  const int head = blockIdx.x;
+  const int b = blockIdx.y;
+  const int q = threadIdx.x % Q, j = threadIdx.x / Q;
+  const int kv_end = visible_end(p, b);
+  // live splits: contiguous slices of `chunk` keys, or (interleaved) one tile each round
+  const int n = p.interleave ? min(p.n_split, (kv_end + kTile16 - 1) / kTile16)
+                             : (kv_end + p.chunk - 1) / p.chunk;
+  const size_t base = (size_t)(b * p.h_q + head) * p.n_split_cap;
+  auto fold = [](float& M, float& L, float4& U, float ms, float ls, float4 us) {
+    if (ms == -INFINITY) return;
+    const float Mn = fmaxf(M, ms);
+    const float a = fast_exp2(M - Mn);       // 0 on the first live state
+    const float w = fast_exp2(ms - Mn);
+    L = a * L + w * ls;
+    U = make_float4(a * U.x + w * us.x, a * U.y + w * us.y, a * U.z + w * us.z, a * U.w + w * us.w);
+    M = Mn;
+  };
+  float M = -INFINITY, L = 0.f;
+  float4 U = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = j; s0 < n; s0 += 8 * NJ) {
+    float ms[8], ls[8];
+    float4 us[8];
+    // unconditional loads (a split past n re-reads split n - 1 and is dropped) keep
+    // all eight requests in flight together
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int sp = min(s0 + k * NJ, n - 1);
+      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + (base + sp) * 2);
+      ms[k] = s0 + k * NJ < n ? ml.x : -INFINITY;
+      ls[k] = ml.y;
+      us[k] = *reinterpret_cast<const float4*>(p.ws_u + (base + sp) * D + 4 * q);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) fold(M, L, U, ms[k], ls[k], us[k]);
+  }
+  st_u[j][q] = U;
+  st_ml[j][q] = make_float2(M, L);
+  __syncthreads();
+  if (j != 0) return;
+  float Mt = -INFINITY, Lt = 0.f;
+  float4 Ut = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) fold(Mt, Lt, Ut, st_ml[jj][q].x, st_ml[jj][q].y, st_u[jj][q]);
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  const size_t oi = (size_t)(b * p.h_q + head) * D + 4 * q;
+  if constexpr (OUT_BF16) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 w4;
+    w4[0] = (__bf16)(Ut.x * inv); w4[1] = (__bf16)(Ut.y * inv); w4[2] = (__bf16)(Ut.z * inv); w4[3] = (__bf16)(Ut.w * inv);
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + oi) = w4;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.o) + oi) = make_float4(Ut.x * inv, Ut.y * inv, Ut.z * inv, Ut.w * inv);
+  }
+}
+
 template <int D, bool OUT_BF16>
 hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
   if (prm.r <= 16) {
@@ -640,7 +707,10 @@ hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.direct) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(prm.h_q, B), dim3(256), 0, s, prm);
+  if (prm.n_split > kManySplits)
+    hipLaunchKernelGGL((decode_combine_many_kernel<D, OUT_BF16>), dim3(prm.h_q, B), dim3(256), 0, s, prm);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(prm.h_q, B), dim3(256), 0, s, prm);
   return hipGetLastError();
 }
 

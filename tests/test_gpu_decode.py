@@ -43,6 +43,7 @@ DECODE_CASES = [
     ("bf16", 2, 12, 4, 257, 128, [257, 129]),         # r=3, lengths straddling tiles
     ("bf16", 4, 32, 8, 9000, 128, [9000, 8192, 4097, 33]),
     ("bf16", 1, 16, 1, 9000, 128, [9000]),            # r=16 on the 16x16 kernel, 36 splits
+    ("bf16", 1, 8, 1, 6000, 64, [6000]),              # d_h 64, 24 splits (batched merge)
     ("f32", 3, 8, 2, 300, 40, [300, 151, 1]),
     ("f32", 1, 32, 1, 100, 128, [100]),
 ]
