@@ -31,6 +31,12 @@ int check_types(int in_dtype, int out_dtype, int d_h) {
 
 bool known_dtype(int t) { return t == GQA_F32 || t == GQA_BF16; }
 
+// The bf16 prefill and backward kernels address the rows of one (sequence, head)
+// through 32-bit buffer offsets: rows * d_h bf16 values must fit in 2^31 - 1 bytes.
+bool bf16_rows_fit(int in_dtype, int rows, int d_h) {
+  return in_dtype != GQA_BF16 || (long long)rows * d_h * 2 <= 0x7fffffffLL;
+}
+
 int check_ptrs(int in_dtype, int out_dtype, const void* q, const void* k, const void* v, const void* o) {
   if (!q || !k || !v || !o) return GQA_ERR_INVALID_ARGUMENT;
   const uintptr_t in_al = in_dtype == GQA_BF16 ? 16 : 4;
@@ -66,6 +72,7 @@ int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
   if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return GQA_ERR_UNSUPPORTED;
   int st = check_types(in_dtype, out_dtype, d_h);
   if (st != GQA_OK) return st;
+  if (!bf16_rows_fit(in_dtype, T_cap, d_h)) return GQA_ERR_UNSUPPORTED;
   st = check_ptrs(in_dtype, out_dtype, q, k_cache, v_cache, o);
   if (st != GQA_OK) return st;
   if ((kv_lens && !aligned(kv_lens, 4)) || (q_pos0 && !aligned(q_pos0, 4))) return GQA_ERR_INVALID_ARGUMENT;
@@ -90,6 +97,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return GQA_ERR_UNSUPPORTED;
   int st = check_types(in_dtype, out_dtype, d_h);
   if (st != GQA_OK) return st;
+  if (!bf16_rows_fit(in_dtype, T, d_h)) return GQA_ERR_UNSUPPORTED;
   st = check_ptrs(in_dtype, out_dtype, q, k, v, o);
   if (st != GQA_OK) return st;
   if (kv_lens && !aligned(kv_lens, 4)) return GQA_ERR_INVALID_ARGUMENT;
@@ -137,6 +145,7 @@ int gqa_prefill_backward(const void* q, const void* k, const void* v, const void
   if (!scale_ok(scale)) return GQA_ERR_INVALID_ARGUMENT;
   if (!known_dtype(in_dtype) || !known_dtype(o_dtype)) return GQA_ERR_UNSUPPORTED;
   if (in_dtype != GQA_BF16 || (d_h != 64 && d_h != 128)) return GQA_ERR_UNSUPPORTED;
+  if (!bf16_rows_fit(in_dtype, T, d_h)) return GQA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) ||
       !aligned(o, o_dtype == GQA_BF16 ? 2 : 4) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||

@@ -43,7 +43,10 @@
  *   - Supported: in_dtype GQA_F32 with out_dtype GQA_F32 for 1 <= d_h <= 256
  *     (reference-precision path); in_dtype GQA_BF16 with out_dtype GQA_F32 or
  *     GQA_BF16 for d_h in {64, 128} (matrix-core path, fp32 accumulation).
- *     Anything else returns GQA_ERR_UNSUPPORTED.
+ *     On the bf16 path of the prefill calls one (sequence, K/V head) of K or V
+ *     must span at most 2^31 - 1 bytes: T_cap * d_h * 2 <= 2147483647
+ *     (T_cap <= 8,388,607 at d_h 128), as the kernels address it with 32-bit
+ *     buffer offsets.  Anything else returns GQA_ERR_UNSUPPORTED.
  *   - Alignment: bf16 tensors and fp32 outputs of the bf16 path need 16-byte
  *     aligned base pointers; fp32 tensors need 4-byte alignment.
  */
@@ -213,7 +216,8 @@ size_t gqa_prefill_backward_workspace_bytes(int B, int h_q, int T);
  * written (zeros for keys no row can see).
  *   workspace: at least gqa_prefill_backward_workspace_bytes(B, h_q, T) bytes,
  *     4-byte aligned; contents need no initialisation.
- * Supported: in_dtype GQA_BF16 with d_h in {64, 128}; otherwise UNSUPPORTED.
+ * Supported: in_dtype GQA_BF16 with d_h in {64, 128} and T * d_h * 2 <=
+ * 2147483647 (32-bit offsets within one head); otherwise UNSUPPORTED.
  * Errors: as gqa_prefill for sizes, mask and scale; INVALID_ARGUMENT for a NULL
  * pointer or misalignment (bf16 tensors and gradients 16-byte aligned);
  * WORKSPACE_TOO_SMALL.

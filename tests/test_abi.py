@@ -63,6 +63,8 @@ FAKE = 0x1000  # never dereferenced: validation fails before any launch
     ((1, 4, 2, 8, 300, 1, 0.1, 0, 0), ops.GQA_ERR_UNSUPPORTED),          # fp32 d_h > 256
     ((1, 4, 2, 8, 64, 1, 0.1, 0, 1), ops.GQA_ERR_UNSUPPORTED),           # fp32 in, bf16 out
     ((1, 4, 2, 8, 64, 1, 0.1, 5, 0), ops.GQA_ERR_UNSUPPORTED),           # unknown dtype
+    ((1, 4, 2, 1 << 23, 128, 1, 0.1, 1, 0), ops.GQA_ERR_UNSUPPORTED),    # one bf16 K head > 2^31 - 1 bytes
+    ((1, 4, 2, 1 << 24, 64, 1, 0.1, 1, 0), ops.GQA_ERR_UNSUPPORTED),
 ])
 def test_prefill_validation(args, expect):
     lib = ops.load_library()
@@ -179,3 +181,16 @@ def test_backward_validation():
         ops.GQA_ERR_INVALID_ARGUMENT
     assert lib.gqa_prefill_lse(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == \
         ops.GQA_ERR_INVALID_ARGUMENT
+
+
+@needs_lib
+def test_bf16_rows_limit_on_chunk_and_backward():
+    """The bf16 prefill kernels address one (sequence, head) with 32-bit offsets: chunked
+    prefill and the backward reject a head span of more than 2^31 - 1 bytes up front."""
+    lib = ops.load_library()
+    big = 1 << 23   # 2^23 rows x 128 x 2 bytes = 2^31
+    assert lib.gqa_prefill_chunk(FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, big, 128, 1, None, None, 0.1,
+                                 ops.GQA_BF16, ops.GQA_F32, None) == ops.GQA_ERR_UNSUPPORTED
+    ws = lib.gqa_prefill_backward_workspace_bytes(1, 4, big)
+    assert lib.gqa_prefill_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, big, 128, 1, None,
+                                    0.1, ops.GQA_BF16, ops.GQA_F32, FAKE, ws, None) == ops.GQA_ERR_UNSUPPORTED
