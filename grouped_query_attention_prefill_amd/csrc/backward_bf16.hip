@@ -90,7 +90,7 @@ bwd_delta_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvLds {
-  static constexpr int TS = D * 2 + 32;            // tile row stride (transposing reads conflict-free)
+  static constexpr int TS = D * 2 + 32;            // tile row stride, bytes
   static constexpr int TILE = kQTile * TS;
   static constexpr int REGION = 2 * TILE + 2 * kQTile * 4;   // Q tile, dO tile, L, delta
   static constexpr int STAGING = 2 * 2 * REGION;             // two parities x two stages

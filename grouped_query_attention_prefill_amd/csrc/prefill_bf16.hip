@@ -36,9 +36,11 @@
 // Layouts in LDS, both filled by 16-byte buffer loads that return zeros past the
 // last visible key (no per-load branches):
 //   K [64 keys][d_h] row-major, rows padded by 16 bytes: 16-byte operand reads
-//     are conflict-free at this stride
-//   V [64 keys][d_h] row-major, rows padded by 32 bytes (conflict-free transposing
-//     reads, which hand the PV product its V^T operand directly).
+//     are conflict-free at this stride (at 32 bytes of padding they take twice
+//     the cycles)
+//   V [64 keys][d_h] row-major, rows padded by 32 bytes, read with transposing
+//     reads that hand the PV product its V^T operand directly (those cost the
+//     same at every stride and layout measured).
 #include <type_traits>
 
 #include "internal.h"
