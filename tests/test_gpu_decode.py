@@ -79,6 +79,31 @@ def test_decode_zero_length_writes_zeros():
     check_parity(got[1:], _oracle_decode(xx, "bf16"), mode="bf16", what="len 0")
 
 
+@pytest.mark.parametrize("h_q,h_kv", [(16, 2), (64, 2)], ids=["r8_16x16", "r32_wide"])
+def test_decode_longest_first_order(h_q, h_kv):
+    """Workgroups take the sequences in order of visible length, longest first: a batch
+    with equal lengths, a zero length and a spread of lengths matches the oracle on
+    both kernels, and the zero-length sequence is written as zeros."""
+    lens = [5000, 1, 0, 4096, 4096, 77, 2500, 5000, 640, 3333, 12, 4999]
+    print(f"case decode longest-first h_q={h_q} h_kv={h_kv}", flush=True)
+    x = inputs.make_decode(len(lens), h_q, h_kv, 128, 5000, "bf16", 11600 + h_q, seq_lens=lens, poison=True)
+    got = _decode(x, "bf16")
+    assert np.all(got[2] == 0.0)
+    keep = [i for i, n in enumerate(lens) if n > 0]
+    xx = {k: (v[keep] if hasattr(v, "shape") and v.shape[:1] == (len(lens),) else v) for k, v in x.items()}
+    check_parity(got[keep], _oracle_decode(xx, "bf16"), mode="bf16", what="longest-first")
+
+
+def test_decode_large_batch_natural_order():
+    """More sequences than a workgroup has threads: grid order is kept (no ranking)."""
+    rng = np.random.Generator(np.random.PCG64(11700))
+    B = 300
+    lens = rng.integers(1, 200, size=B, endpoint=True).astype(np.int32)
+    print(f"case decode B={B} natural order", flush=True)
+    x = inputs.make_decode(B, 8, 2, 64, 200, "bf16", 11700, seq_lens=lens, poison=True)
+    check_parity(_decode(x, "bf16"), _oracle_decode(x, "bf16"), mode="bf16", what="B=300")
+
+
 def test_decode_equals_last_prefill_row_bf16():
     import torch
 
