@@ -513,16 +513,11 @@ hipError_t launch_t(const BwdParams& prm, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  static bool attr = false;
-  if (!attr) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, DkdvLds<D>::TOTAL);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel<D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, DqLds<D>::TOTAL);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<unsigned long long> dkdv_allowed{0}, dq_allowed{0};
+  e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>), DkdvLds<D>::TOTAL, dkdv_allowed);
+  if (e != hipSuccess) return e;
+  e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dq_kernel<D>), DqLds<D>::TOTAL, dq_allowed);
+  if (e != hipSuccess) return e;
   const int n_kb = (prm.T + kKeyBlock - 1) / kKeyBlock;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(prm.B * prm.h_kv * n_kb)), dim3(kBwdThreads),
                      DkdvLds<D>::TOTAL, s, prm);

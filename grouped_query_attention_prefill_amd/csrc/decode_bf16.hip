@@ -714,24 +714,18 @@ template <int D, bool OUT_BF16>
 hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
   if (prm.r <= 16) {
     constexpr int smem = Decode16Lds<D>::TOTAL;
-    static bool attr16 = false;
-    if (!attr16) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode16_bf16_kernel<D, OUT_BF16>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-      if (e != hipSuccess) return e;
-      attr16 = true;
-    }
+    static std::atomic<unsigned long long> lds_allowed{0};
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(decode16_bf16_kernel<D, OUT_BF16>), smem,
+                                           lds_allowed);
+    if (e != hipSuccess) return e;
     dim3 grid(prm.n_split, prm.h_kv, B);
     hipLaunchKernelGGL((decode16_bf16_kernel<D, OUT_BF16>), grid, dim3(kThreads), smem, s, prm);
   } else {
     constexpr int smem = DecodeLds<D>::TOTAL;
-    static bool attr32 = false;
-    if (!attr32) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_bf16_kernel<D, OUT_BF16>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-      if (e != hipSuccess) return e;
-      attr32 = true;
-    }
+    static std::atomic<unsigned long long> lds_allowed{0};
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(decode_bf16_kernel<D, OUT_BF16>), smem,
+                                           lds_allowed);
+    if (e != hipSuccess) return e;
     dim3 grid(prm.n_split, prm.h_kv * prm.hc_count, B);
     hipLaunchKernelGGL((decode_bf16_kernel<D, OUT_BF16>), grid, dim3(kThreads), smem, s, prm);
   }

@@ -2,11 +2,28 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
 
 namespace gqa {
+
+// Kernels with more than 64 KiB of dynamic LDS have to be allowed it
+// (hipFuncSetAttribute) on each device they run on.  `done` records the devices
+// already allowed, one bit per device ordinal below 64 (other ordinals are set on
+// every call); two threads racing on a first call both set the attribute, which
+// is harmless.
+inline hipError_t allow_dynamic_lds(const void* fn, int bytes, std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Attention over a cache for S_q query rows per sequence at absolute positions
 // q_pos0[b] + i.  Prefill is the case q_pos0 = 0, S_q = T_cap.

@@ -372,13 +372,10 @@ prefill_bf16_kernel(PrefillParams p) {
 template <int D, bool OUT_BF16>
 hipError_t launch_t(const PrefillParams& prm, int total, hipStream_t s) {
   constexpr int smem = PrefillLds<D>::TOTAL;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_bf16_kernel<D, OUT_BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static std::atomic<unsigned long long> lds_allowed{0};
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(prefill_bf16_kernel<D, OUT_BF16>), smem,
+                                         lds_allowed);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16>), dim3(total), dim3(kThreads), smem, s, prm);
   return hipGetLastError();
 }
