@@ -135,6 +135,17 @@ def _int_vec(t, name, B, device):
     return t
 
 
+def _launch(device, tensors, fn, *args) -> None:
+    """Call a C entry point with ``device`` current and its current stream as the
+    trailing stream argument; every tensor argument must live on ``device``."""
+    torch = _torch()
+    for name, t in tensors:
+        if t is not None:
+            _require(t.device == device, f"{name} must be on {device}")
+    with torch.cuda.device(device):
+        _check(fn(*args, _stream_handle(device)))
+
+
 def _out_code(in_code: int, out_dtype) -> int:
     if out_dtype is None:
         return GQA_F32
@@ -166,9 +177,9 @@ def gqa_prefill(q, k, v, *, causal: bool = True, scale: Optional[float] = None, 
     kv_lens = _int_vec(kv_lens, "kv_lens", B, q.device)
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
     lib = load_library()
-    _check(lib.gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h_q, h_kv, T, d_h,
-                           GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc,
-                           code, oc, _stream_handle(q.device)))
+    _launch(q.device, (("k", k), ("v", v), ("out", out)), lib.gqa_prefill,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h_q, h_kv, T, d_h,
+            GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc, code, oc)
     return out
 
 
@@ -193,9 +204,9 @@ def gqa_prefill_chunk(q, k_cache, v_cache, *, kv_lens=None, q_pos0=None, causal:
     q_pos0 = _int_vec(q_pos0, "q_pos0", B, q.device)
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
     lib = load_library()
-    _check(lib.gqa_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, h_q, h_kv, S_q,
-                                 T_cap, d_h, GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens),
-                                 _ptr(q_pos0), sc, code, oc, _stream_handle(q.device)))
+    _launch(q.device, (("k_cache", k_cache), ("v_cache", v_cache), ("out", out)), lib.gqa_prefill_chunk,
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, h_q, h_kv, S_q, T_cap, d_h,
+            GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), _ptr(q_pos0), sc, code, oc)
     return out
 
 
@@ -232,9 +243,9 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, *, q_pos=None, scale: Optional[flo
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
     msl = 0 if max_seq_len is None else int(max_seq_len)
-    _check(lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(q_pos), _ptr(out),
-                          B, h_q, h_kv, T_cap, d_h, msl, sc, code, oc, _ptr(workspace), ws_have,
-                          _stream_handle(q.device)))
+    _launch(q.device, (("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("workspace", workspace)),
+            lib.gqa_decode, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(q_pos), _ptr(out),
+            B, h_q, h_kv, T_cap, d_h, msl, sc, code, oc, _ptr(workspace), ws_have)
     return out
 
 
@@ -250,8 +261,9 @@ def gqa_kv_append(k_cache, v_cache, k_new, v_new, write_pos):
     write_pos = _int_vec(write_pos, "write_pos", B, k_cache.device)
     _require(write_pos is not None, "write_pos is required")
     lib = load_library()
-    _check(lib.gqa_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(write_pos),
-                             B, h_kv, T_cap, d_h, _dtype_code(k_cache), _stream_handle(k_cache.device)))
+    _launch(k_cache.device, (("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)), lib.gqa_kv_append,
+            _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(write_pos),
+            B, h_kv, T_cap, d_h, _dtype_code(k_cache))
     return k_cache, v_cache
 
 
@@ -285,9 +297,11 @@ def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, q_pos=None, 
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
     msl = 0 if max_seq_len is None else int(max_seq_len)
-    _check(lib.gqa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(q_pos),
-                                _ptr(out), B, h_q, h_kv, page_size, n_pages, max_pages, d_h, msl, sc, code, oc,
-                                _ptr(workspace), ws_have, _stream_handle(q.device)))
+    _launch(q.device, (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table), ("out", out),
+                       ("workspace", workspace)),
+            lib.gqa_decode_paged, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
+            _ptr(q_pos), _ptr(out), B, h_q, h_kv, page_size, n_pages, max_pages, d_h, msl, sc, code, oc,
+            _ptr(workspace), ws_have)
     return out
 
 
@@ -306,9 +320,9 @@ def gqa_kv_append_paged(k_pages, v_pages, k_new, v_new, block_table, write_pos):
     write_pos = _int_vec(write_pos, "write_pos", B, k_pages.device)
     _require(write_pos is not None, "write_pos is required")
     lib = load_library()
-    _check(lib.gqa_kv_append_paged(_ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new), _ptr(block_table),
-                                   _ptr(write_pos), B, h_kv, page_size, n_pages, block_table.shape[1], d_h,
-                                   _dtype_code(k_pages), _stream_handle(k_pages.device)))
+    _launch(k_pages.device, (("v_pages", v_pages), ("k_new", k_new), ("v_new", v_new), ("block_table", block_table)),
+            lib.gqa_kv_append_paged, _ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new), _ptr(block_table),
+            _ptr(write_pos), B, h_kv, page_size, n_pages, block_table.shape[1], d_h, _dtype_code(k_pages))
     return k_pages, v_pages
 
 
@@ -328,8 +342,8 @@ def gqa_rope(x, *, pos0=None, base: float = ROPE_BASE, out=None):
     _dev_tensor(out, "out", 4)
     _require(out.shape == x.shape and out.dtype == x.dtype, "out must match x")
     pos0 = _int_vec(pos0, "pos0", B, x.device)
-    _check(load_library().gqa_rope(_ptr(x), _ptr(out), _ptr(pos0), B, H, S, d_h, float(base), _dtype_code(x),
-                                   _stream_handle(x.device)))
+    _launch(x.device, (("out", out),), load_library().gqa_rope,
+            _ptr(x), _ptr(out), _ptr(pos0), B, H, S, d_h, float(base), _dtype_code(x))
     return out
 
 
@@ -344,9 +358,9 @@ def gqa_kv_append_rope(k_cache, v_cache, k_new, v_new, write_pos, *, base: float
     _require(k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype, "dtypes must match")
     write_pos = _int_vec(write_pos, "write_pos", B, k_cache.device)
     _require(write_pos is not None, "write_pos is required")
-    _check(load_library().gqa_kv_append_rope(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
-                                             _ptr(write_pos), B, h_kv, T_cap, d_h, float(base),
-                                             _dtype_code(k_cache), _stream_handle(k_cache.device)))
+    _launch(k_cache.device, (("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)),
+            load_library().gqa_kv_append_rope, _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+            _ptr(write_pos), B, h_kv, T_cap, d_h, float(base), _dtype_code(k_cache))
     return k_cache, v_cache
 
 
@@ -372,9 +386,9 @@ def gqa_prefill_lse(q, k, v, *, causal: bool = True, scale: Optional[float] = No
     _require(lse.dtype == torch.float32 and tuple(lse.shape) == (B, h_q, T), "lse must be fp32 (B, h_q, T)")
     kv_lens = _int_vec(kv_lens, "kv_lens", B, q.device)
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
-    _check(load_library().gqa_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, h_q, h_kv, T, d_h,
-                                          GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc,
-                                          code, oc, _stream_handle(q.device)))
+    _launch(q.device, (("k", k), ("v", v), ("out", out), ("lse", lse)), load_library().gqa_prefill_lse,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, h_q, h_kv, T, d_h,
+            GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc, code, oc)
     return out, lse
 
 
@@ -411,8 +425,9 @@ def gqa_prefill_backward(q, k, v, o, d_o, lse, *, causal: bool = True, scale: Op
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_have = workspace.numel() * workspace.element_size()
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
-    _check(lib.gqa_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
-                                    _ptr(dv), B, h_q, h_kv, T, d_h, GQA_MASK_CAUSAL if causal else GQA_MASK_NONE,
-                                    _ptr(kv_lens), sc, _dtype_code(q), _dtype_code(o), _ptr(workspace), ws_have,
-                                    _stream_handle(q.device)))
+    _launch(q.device, (("k", k), ("v", v), ("o", o), ("d_o", d_o), ("lse", lse), ("dq", dq), ("dk", dk),
+                       ("dv", dv), ("workspace", workspace)),
+            lib.gqa_prefill_backward, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
+            _ptr(dv), B, h_q, h_kv, T, d_h, GQA_MASK_CAUSAL if causal else GQA_MASK_NONE,
+            _ptr(kv_lens), sc, _dtype_code(q), _dtype_code(o), _ptr(workspace), ws_have)
     return dq, dk, dv

@@ -30,8 +30,12 @@
  *     (B, h_kv, T, d_h).  Integer arrays are device int32.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL means the default stream).  Calls return once enqueued.
- *   - The library allocates no device memory and keeps no state between
- *     calls; calls on different streams are independent.
+ *     The stream belongs to the calling thread's current device, the device
+ *     every pointer refers to.
+ *   - The library allocates no device memory.  Its only state is a per-device
+ *     record that its kernels with more than 64 KiB of LDS have been allowed
+ *     it (set on the first call on each device, safe under concurrent first
+ *     calls); calls on different streams are independent.
  *   - Host-checkable argument errors return a status before any launch and
  *     leave every output untouched.  Launch failures return GQA_ERR_HIP.
  *   - Data conditions that only the device can see have defined results:

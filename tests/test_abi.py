@@ -194,3 +194,13 @@ def test_bf16_rows_limit_on_chunk_and_backward():
     ws = lib.gqa_prefill_backward_workspace_bytes(1, 4, big)
     assert lib.gqa_prefill_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, big, 128, 1, None,
                                     0.1, ops.GQA_BF16, ops.GQA_F32, FAKE, ws, None) == ops.GQA_ERR_UNSUPPORTED
+
+
+def test_binding_requires_one_device_for_every_tensor():
+    """The binding checks that every tensor argument lives on the device it makes
+    current for the call, before anything reaches the library."""
+    torch = pytest.importorskip("torch")
+    called = []
+    with pytest.raises(ValueError, match="k must be on cuda:0"):
+        ops._launch(torch.device("cuda:0"), (("k", torch.empty(1)),), lambda *a: called.append(a) or 0)
+    assert not called
