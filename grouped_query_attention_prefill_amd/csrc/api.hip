@@ -1,6 +1,7 @@
 // C ABI of the grouped-query attention library: argument validation and
 // dispatch to the kernels.  Every host-checkable error is reported before any
-// launch; nothing is allocated and no state is kept between calls.
+// launch; nothing is allocated, and the only state kept between calls is the
+// per-device record of kernels allowed more than 64 KiB of LDS.
 #include "gqa.h"
 #include "internal.h"
 
