@@ -234,13 +234,14 @@ def bench_decode(name, steps, warmup, flush_buf, page_size=0):
     else:
         dec = lambda: ops.gqa_decode(qd, kd, vd, sl, q_pos=qp, max_seq_len=msl, out=out, workspace=ws)
     if appended:
+        # one call per step: the decode kernel writes the new rows and reads them in place
         kn, vn, wp = to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints(x["write_pos"])
-        app = (lambda: ops.gqa_kv_append_paged(kd, vd, kn, vn, bt, wp)) if page_size else \
-            (lambda: ops.gqa_kv_append(kd, vd, kn, vn, wp))
-
-        def fn():
-            app()
-            dec()
+        if page_size:
+            fn = lambda: ops.gqa_append_decode_paged(qd, kd, vd, kn, vn, bt, wp, sl, q_pos=qp, max_seq_len=msl,
+                                                     out=out, workspace=ws)
+        else:
+            fn = lambda: ops.gqa_append_decode(qd, kd, vd, kn, vn, wp, sl, q_pos=qp, max_seq_len=msl, out=out,
+                                               workspace=ws)
     else:
         fn = dec
     # read (not write) a buffer larger than the Infinity Cache: evicts the inputs
@@ -259,7 +260,7 @@ def bench_decode(name, steps, warmup, flush_buf, page_size=0):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("decode_bf16_kernel", wname)},
-        "kernels": ("kv_append + " if appended else "") + "decode split + combine",
+        "kernels": "decode split (append fused) + combine" if appended else "decode split + combine",
     }
     if page_size:
         res["page_size"] = page_size

@@ -174,11 +174,28 @@ size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int T_cap, int d_h, 
   return gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, T_cap).workspace_bytes;
 }
 
-int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
-               const int32_t* seq_lens, const int32_t* q_pos, void* o,
-               int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
-               float scale, int in_dtype, int out_dtype,
-               void* workspace, size_t workspace_bytes, void* stream) {
+// The new token's rows for the fused append + decode calls.
+struct AppendIn {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* write_pos;
+};
+
+// kv_append's pointer rules: 16-byte rows need 16-byte aligned bases.
+static bool append_ptrs_ok(const AppendIn& ap, const void* k_cache, const void* v_cache, int d_h, int eb) {
+  if (!ap.k_new || !ap.v_new || !ap.write_pos || !aligned(ap.write_pos, 4)) return false;
+  const uintptr_t al = (d_h * eb) % 16 == 0 ? 16 : (uintptr_t)eb;
+  return aligned(ap.k_new, al) && aligned(ap.v_new, al) && aligned(k_cache, al) && aligned(v_cache, al);
+}
+
+// Decode over a contiguous cache, after an optional append (ap non-null).  Every
+// check runs before the first launch.  The bf16 path with r <= 16 writes the new
+// row inside the decode kernel; the other paths launch kv_append first.
+static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                       int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+                       float scale, int in_dtype, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream, const AppendIn* ap) {
   if (B < 1 || h_q < 1 || h_kv < 1 || T_cap < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (max_seq_len > T_cap) return GQA_ERR_INVALID_ARGUMENT;
@@ -189,6 +206,8 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   st = check_ptrs(in_dtype, out_dtype, q, k_cache, v_cache, o);
   if (st != GQA_OK) return st;
   if (!seq_lens || !aligned(seq_lens, 4) || (q_pos && !aligned(q_pos, 4))) return GQA_ERR_INVALID_ARGUMENT;
+  const int eb = in_dtype == GQA_BF16 ? 2 : 4;
+  if (ap && !append_ptrs_ok(*ap, k_cache, v_cache, d_h, eb)) return GQA_ERR_INVALID_ARGUMENT;
   const int len = max_seq_len > 0 ? max_seq_len : T_cap;
   DecodeArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.q_pos = q_pos; a.o = o;
@@ -197,20 +216,31 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (in_dtype == GQA_F32) return hip_status(gqa::launch_decode_f32(a, s));
-  const gqa::DecodePlan pl = gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, len);
-  if (pl.n_split > 1) {
-    if (workspace_bytes < pl.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
-    if (!workspace || !aligned(workspace, 16)) return GQA_ERR_INVALID_ARGUMENT;
+  gqa::DecodePlan pl{};
+  if (in_dtype == GQA_BF16) {
+    pl = gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, len);
+    if (pl.n_split > 1) {
+      if (workspace_bytes < pl.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+      if (!workspace || !aligned(workspace, 16)) return GQA_ERR_INVALID_ARGUMENT;
+    }
   }
+  const bool fused = ap && in_dtype == GQA_BF16 && h_q / h_kv <= 16;
+  if (ap && !fused) {
+    const hipError_t e = gqa::launch_kv_append(const_cast<void*>(k_cache), const_cast<void*>(v_cache), ap->k_new,
+                                               ap->v_new, ap->write_pos, B, h_kv, T_cap, d_h, eb, s);
+    if (e != hipSuccess) return GQA_ERR_HIP;
+  }
+  if (fused) { a.k_new = ap->k_new; a.v_new = ap->v_new; a.write_pos = ap->write_pos; }
+  if (in_dtype == GQA_F32) return hip_status(gqa::launch_decode_f32(a, s));
   return hip_status(gqa::launch_decode_bf16(a, pl, s));
 }
 
-int gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
-                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos, void* o,
-                     int B, int h_q, int h_kv, int page_size, int n_pages, int max_pages_per_seq, int d_h,
-                     int max_seq_len, float scale, int in_dtype, int out_dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+// Decode over a paged cache, after an optional append (ap non-null).
+static int decode_paged_impl(const void* q, const void* k_pages, const void* v_pages,
+                             const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                             int B, int h_q, int h_kv, int page_size, int n_pages, int max_pages_per_seq, int d_h,
+                             int max_seq_len, float scale, int in_dtype, int out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream, const AppendIn* ap) {
   if (B < 1 || h_q < 1 || h_kv < 1 || page_size < 1 || n_pages < 1 || max_pages_per_seq < 1 || d_h < 1)
     return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
@@ -227,6 +257,7 @@ int gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
   if (st != GQA_OK) return st;
   if (!block_table || !seq_lens || !aligned(block_table, 4) || !aligned(seq_lens, 4) || (q_pos && !aligned(q_pos, 4)))
     return GQA_ERR_INVALID_ARGUMENT;
+  if (ap && !append_ptrs_ok(*ap, k_pages, v_pages, d_h, 2)) return GQA_ERR_INVALID_ARGUMENT;
   const int len = max_seq_len > 0 ? max_seq_len : T_cap;
   DecodeArgs a;
   a.q = q; a.k = k_pages; a.v = v_pages; a.seq_lens = seq_lens; a.q_pos = q_pos; a.o = o;
@@ -240,7 +271,56 @@ int gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
     if (workspace_bytes < pl.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
     if (!workspace || !aligned(workspace, 16)) return GQA_ERR_INVALID_ARGUMENT;
   }
-  return hip_status(gqa::launch_decode_bf16(a, pl, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = ap && h_q / h_kv <= 16;
+  if (ap && !fused) {
+    const hipError_t e = gqa::launch_kv_append_paged(const_cast<void*>(k_pages), const_cast<void*>(v_pages),
+                                                     ap->k_new, ap->v_new, block_table, ap->write_pos, B, h_kv,
+                                                     page_size, n_pages, max_pages_per_seq, d_h, 2, s);
+    if (e != hipSuccess) return GQA_ERR_HIP;
+  }
+  if (fused) { a.k_new = ap->k_new; a.v_new = ap->v_new; a.write_pos = ap->write_pos; }
+  return hip_status(gqa::launch_decode_bf16(a, pl, s));
+}
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* seq_lens, const int32_t* q_pos, void* o,
+               int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+               float scale, int in_dtype, int out_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, max_seq_len, scale,
+                     in_dtype, out_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int gqa_append_decode(const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      const int32_t* write_pos, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                      int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+                      float scale, int in_dtype, int out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const AppendIn ap{k_new, v_new, write_pos};
+  return decode_impl(q, k_cache, v_cache, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, max_seq_len, scale,
+                     in_dtype, out_dtype, workspace, workspace_bytes, stream, &ap);
+}
+
+int gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                     int B, int h_q, int h_kv, int page_size, int n_pages, int max_pages_per_seq, int d_h,
+                     int max_seq_len, float scale, int in_dtype, int out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_paged_impl(q, k_pages, v_pages, block_table, seq_lens, q_pos, o, B, h_q, h_kv, page_size, n_pages,
+                           max_pages_per_seq, d_h, max_seq_len, scale, in_dtype, out_dtype, workspace,
+                           workspace_bytes, stream, nullptr);
+}
+
+int gqa_append_decode_paged(const void* q, void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                            const int32_t* block_table, const int32_t* write_pos, const int32_t* seq_lens,
+                            const int32_t* q_pos, void* o, int B, int h_q, int h_kv, int page_size, int n_pages,
+                            int max_pages_per_seq, int d_h, int max_seq_len, float scale, int in_dtype,
+                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const AppendIn ap{k_new, v_new, write_pos};
+  return decode_paged_impl(q, k_pages, v_pages, block_table, seq_lens, q_pos, o, B, h_q, h_kv, page_size, n_pages,
+                           max_pages_per_seq, d_h, max_seq_len, scale, in_dtype, out_dtype, workspace,
+                           workspace_bytes, stream, &ap);
 }
 
 int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,

@@ -51,6 +51,11 @@ struct DecodeParams {
   // j % page_size of page block_table[b * max_pages + j / page_size]; null = contiguous
   const int32_t* block_table;
   int page_size, max_pages, n_pages;
+  // fused append (16x16 kernel; write_pos null = none): row write_pos[b] of cache
+  // head (b, g) receives k_new / v_new (B, h_kv, 1, D) before the decode reads it
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* write_pos;
   float c;            // scale * log2(e)
 };
 
@@ -411,6 +416,41 @@ decode16_bf16_kernel(DecodeParams p) {
   const int hi = kv_end;
   const int n_heads_here = p.r;   // <= 16
 
+  // fused append: position wp of (b, g) takes the new row.  Only the split whose
+  // tiles hold wp reads that row, and it takes the new values in place of the
+  // cache's (below, in load_tile); the same split writes the row to the cache
+  // (split 0 when no split reads it).  A position outside the cache, or on a page
+  // outside the pool, is skipped, as by kv_append.
+  int wp = -1;
+  if (p.write_pos) {
+    wp = p.write_pos[b];
+    const int cap = p.block_table ? p.max_pages * p.page_size : p.T_cap;
+    if (wp < 0 || wp >= cap) wp = -1;
+  }
+  if (wp >= 0) {
+    const int tw = wp / kTile16;
+    if (split == (tw < n_all ? tw % p.n_split : 0) && tid < D / 4) {
+      size_t row = ((size_t)(b * p.h_kv + g) * p.T_cap + wp) * D;
+      bool backed = true;
+      if (p.block_table) {
+        const int pg = p.block_table[(size_t)b * p.max_pages + wp / p.page_size];
+        backed = pg >= 0 && pg < p.n_pages;
+        row = (((size_t)pg * p.h_kv + g) * p.page_size + wp % p.page_size) * D;
+      }
+      if (backed) {
+        const int c8 = tid % (D / 8);
+        const size_t src = (size_t)(b * p.h_kv + g) * D + c8 * 8;
+        // the caches are the caller's writable buffers; only this path writes them
+        if (tid < D / 8)
+          *reinterpret_cast<uint4*>(const_cast<uint16_t*>(p.k) + row + c8 * 8) =
+              *reinterpret_cast<const uint4*>(p.k_new + src);
+        else
+          *reinterpret_cast<uint4*>(const_cast<uint16_t*>(p.v) + row + c8 * 8) =
+              *reinterpret_cast<const uint4*>(p.v_new + src);
+      }
+    }
+  }
+
   if (n_tiles == 0) {
     if (p.direct) {
       for (int e = tid; e < n_heads_here * D; e += kThreads) {
@@ -457,6 +497,19 @@ decode16_bf16_kernel(DecodeParams p) {
       const uint32_t off = (uint32_t)(row * D + c8 * 8) * 2;
       kreg[i] = load16(krs, off);
       vreg[i] = load16(vrs, off);
+    }
+    if (wp >= k0 && wp < k0 + kTile16) {
+      // the appended row: new values in place of the cache's
+#pragma unroll
+      for (int i = 0; i < UNITS; ++i) {
+        const int u = tid + kThreads * i;
+        const int row = u / (D / 8), c8 = u % (D / 8);
+        if (k0 + row == wp) {
+          const size_t src = (size_t)(b * p.h_kv + g) * D + c8 * 8;
+          kreg[i] = *reinterpret_cast<const uint4*>(p.k_new + src);
+          vreg[i] = *reinterpret_cast<const uint4*>(p.v_new + src);
+        }
+      }
     }
   };
   auto store_tile = [&]() {
@@ -772,6 +825,7 @@ DecodePlan plan_decode_bf16(int B, int h_q, int h_kv, int T_cap, int D, int len)
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& pl, hipStream_t s) {
+  if (a.write_pos && a.h_q / a.h_kv > 16) return hipErrorInvalidValue;   // fused append: 16x16 kernel only
   DecodeParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -787,6 +841,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.interleave = p.r <= 16 ? 1 : 0;
   p.block_table = a.block_table;
   p.page_size = a.page_size; p.max_pages = a.max_pages; p.n_pages = a.n_pages;
+  p.k_new = static_cast<const uint16_t*>(a.k_new);
+  p.v_new = static_cast<const uint16_t*>(a.v_new);
+  p.write_pos = a.write_pos;
   p.c = a.scale * kLog2e;
   const size_t u_bytes = (size_t)a.B * a.h_q * pl.n_split_cap * a.D * sizeof(float);
   p.ws_u = static_cast<float*>(a.workspace);

@@ -60,6 +60,11 @@ struct DecodeArgs {
   // page_size, D); T_cap = max_pages * page_size
   const int32_t* block_table = nullptr;
   int page_size = 0, max_pages = 0, n_pages = 0;
+  // fused append (write_pos non-null; 16x16 kernel only, r <= 16): k_new, v_new
+  // (B, h_kv, 1, D) written to position write_pos[b] and used by this decode
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* write_pos = nullptr;
 };
 
 struct DecodePlan {

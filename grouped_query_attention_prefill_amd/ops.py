@@ -38,6 +38,9 @@ SIGNATURES = {
     "gqa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "gqa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "gqa_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "gqa_append_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
+    "gqa_append_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                     _I, _I, _P, _S, _P]),
     "gqa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "gqa_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_rope": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
@@ -265,6 +268,96 @@ def gqa_kv_append(k_cache, v_cache, k_new, v_new, write_pos):
             _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(write_pos),
             B, h_kv, T_cap, d_h, _dtype_code(k_cache))
     return k_cache, v_cache
+
+
+def _new_rows(k_new, v_new, B, h_kv, d_h, dtype, device):
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, n, 4)
+        _require(t.device == device, f"{n} must be on {device}")
+    _require(tuple(k_new.shape) == (B, h_kv, 1, d_h) and k_new.shape == v_new.shape,
+             "k_new, v_new must be (B, h_kv, 1, d_h)")
+    _require(k_new.dtype == v_new.dtype == dtype, "k_new, v_new must share the caches' dtype")
+
+
+def gqa_append_decode(q, k_cache, v_cache, k_new, v_new, write_pos, seq_lens, *, q_pos=None,
+                      scale: Optional[float] = None, max_seq_len: Optional[int] = None, out=None, out_dtype=None,
+                      workspace=None):
+    """gqa_kv_append(k_cache, v_cache, k_new, v_new, write_pos) then gqa_decode(...), in one call."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, n, 4)
+    B, h_q, S_q, d_h = q.shape
+    _require(S_q == 1, "decode takes one query per sequence (S_q = 1)")
+    _require(k_cache.shape == v_cache.shape and k_cache.shape[0] == B and k_cache.shape[3] == d_h,
+             "caches must be (B, h_kv, T_cap, d_h)")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q and caches must share a dtype")
+    h_kv, T_cap = k_cache.shape[1], k_cache.shape[2]
+    _new_rows(k_new, v_new, B, h_kv, d_h, q.dtype, q.device)
+    write_pos = _int_vec(write_pos, "write_pos", B, q.device)
+    _require(write_pos is not None, "write_pos is required")
+    code = _dtype_code(q)
+    oc = _out_code(code, out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((B, h_q, 1, d_h), dtype=_torch_dtype(oc), device=q.device)
+    _dev_tensor(out, "out", 4)
+    _require(tuple(out.shape) == (B, h_q, 1, d_h), "out must be (B, h_q, 1, d_h)")
+    seq_lens = _int_vec(seq_lens, "seq_lens", B, q.device)
+    _require(seq_lens is not None, "seq_lens is required")
+    q_pos = _int_vec(q_pos, "q_pos", B, q.device)
+    lib = load_library()
+    ws_bytes = int(lib.gqa_decode_workspace_bytes(B, h_q, h_kv, T_cap, d_h, code))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    msl = 0 if max_seq_len is None else int(max_seq_len)
+    _launch(q.device, (("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("workspace", workspace)),
+            lib.gqa_append_decode, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+            _ptr(write_pos), _ptr(seq_lens), _ptr(q_pos), _ptr(out), B, h_q, h_kv, T_cap, d_h, msl, sc, code, oc,
+            _ptr(workspace), ws_have)
+    return out
+
+
+def gqa_append_decode_paged(q, k_pages, v_pages, k_new, v_new, block_table, write_pos, seq_lens, *, q_pos=None,
+                            scale: Optional[float] = None, max_seq_len: Optional[int] = None, out=None,
+                            out_dtype=None, workspace=None):
+    """gqa_kv_append_paged then gqa_decode_paged on the same page pools, in one call."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        _dev_tensor(t, n, 4)
+    B, h_q, S_q, d_h = q.shape
+    _require(S_q == 1, "decode takes one query per sequence (S_q = 1)")
+    _require(k_pages.shape == v_pages.shape and k_pages.shape[3] == d_h, "pages must be (n_pages, h_kv, page_size, d_h)")
+    _require(q.dtype == k_pages.dtype == v_pages.dtype, "q and pages must share a dtype")
+    n_pages, h_kv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _new_rows(k_new, v_new, B, h_kv, d_h, q.dtype, q.device)
+    _dev_tensor(block_table, "block_table", 2)
+    _require(block_table.dtype == torch.int32 and block_table.shape[0] == B, "block_table must be int32 (B, max_pages)")
+    max_pages = block_table.shape[1]
+    write_pos = _int_vec(write_pos, "write_pos", B, q.device)
+    _require(write_pos is not None, "write_pos is required")
+    code = _dtype_code(q)
+    oc = _out_code(code, out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((B, h_q, 1, d_h), dtype=_torch_dtype(oc), device=q.device)
+    _dev_tensor(out, "out", 4)
+    _require(tuple(out.shape) == (B, h_q, 1, d_h), "out must be (B, h_q, 1, d_h)")
+    seq_lens = _int_vec(seq_lens, "seq_lens", B, q.device)
+    _require(seq_lens is not None, "seq_lens is required")
+    q_pos = _int_vec(q_pos, "q_pos", B, q.device)
+    lib = load_library()
+    ws_bytes = int(lib.gqa_decode_workspace_bytes(B, h_q, h_kv, page_size * max_pages, d_h, code))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    msl = 0 if max_seq_len is None else int(max_seq_len)
+    _launch(q.device, (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table), ("out", out),
+                       ("workspace", workspace)),
+            lib.gqa_append_decode_paged, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new),
+            _ptr(block_table), _ptr(write_pos), _ptr(seq_lens), _ptr(q_pos), _ptr(out), B, h_q, h_kv, page_size,
+            n_pages, max_pages, d_h, msl, sc, code, oc, _ptr(workspace), ws_have)
+    return out
 
 
 def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, q_pos=None, scale: Optional[float] = None,

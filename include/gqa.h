@@ -191,6 +191,36 @@ int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const v
                         int page_size, int n_pages, int max_pages_per_seq, int d_h, int dtype, void* stream);
 
 /*
+ * One decode step in one call: gqa_kv_append(k_cache, v_cache, k_new, v_new,
+ * write_pos) followed by gqa_decode(...) on the same caches, with the same
+ * results (the pages' decode step appends the new token's K and V, then
+ * attends over every visible row: [AttnVar] 3.1; [MhaMqaGqa] section 4).  On
+ * the bf16 path with r = h_q / h_kv <= 16 the decode kernel itself writes the
+ * new rows and uses them where it reads row write_pos[b], saving the append's
+ * launch; otherwise the two run as two launches.  Arguments as gqa_decode and
+ * gqa_kv_append (k_new, v_new (B, h_kv, 1, d_h) in_dtype, write_pos (B,)
+ * int32; a write_pos outside [0, T_cap) skips that sequence's append).
+ * Errors: those of both calls, all checked before anything is launched.
+ */
+int gqa_append_decode(const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      const int32_t* write_pos, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                      int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+                      float scale, int in_dtype, int out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same step on a paged cache: gqa_kv_append_paged followed by
+ * gqa_decode_paged, fused in the same way (an append whose page index is
+ * outside the pool is skipped, and its row stays invisible).  Arguments and
+ * errors as those two calls.
+ */
+int gqa_append_decode_paged(const void* q, void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                            const int32_t* block_table, const int32_t* write_pos, const int32_t* seq_lens,
+                            const int32_t* q_pos, void* o, int B, int h_q, int h_kv, int page_size, int n_pages,
+                            int max_pages_per_seq, int d_h, int max_seq_len, float scale, int in_dtype,
+                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gqa_prefill that also writes the row log-sum-exp of the scaled scores,
  * lse[b][a][i] = log sum_j exp(scale q_i . k_j) over the visible keys (natural
  * log; -inf for a row with no visible key), fp32 (B, h_q, T).  These per-row

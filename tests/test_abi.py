@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
               "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged",
               "gqa_rope", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
-              "gqa_prefill_backward_workspace_bytes"):
+              "gqa_prefill_backward_workspace_bytes", "gqa_append_decode", "gqa_append_decode_paged"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -204,3 +204,50 @@ def test_binding_requires_one_device_for_every_tensor():
     with pytest.raises(ValueError, match="k must be on cuda:0"):
         ops._launch(torch.device("cuda:0"), (("k", torch.empty(1)),), lambda *a: called.append(a) or 0)
     assert not called
+
+
+@needs_lib
+def test_append_decode_validation():
+    """The fused append + decode calls check the arguments of both calls before
+    anything is launched (every case here fails a host check)."""
+    lib = ops.load_library()
+    ws = lib.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128, ops.GQA_BF16)
+    names = ["q", "kc", "vc", "kn", "vn", "wp", "sl", "qp", "o", "B", "h_q", "h_kv", "T", "d_h", "msl", "scale",
+             "in", "out", "ws", "wsb", "stream"]
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 32, 8, 8192, 128, 0, 0.088, ops.GQA_BF16,
+            ops.GQA_F32, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.gqa_append_decode(*a)
+
+    assert call(kn=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(vn=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(wp=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(kn=FAKE + 8) == ops.GQA_ERR_INVALID_ARGUMENT        # new rows need 16-byte alignment
+    assert call(wp=FAKE + 2) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(sl=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(msl=8193) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(h_q=30) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call(wsb=ws - 1) == ops.GQA_ERR_WORKSPACE_TOO_SMALL
+    assert call(B=2, h_q=256, wsb=0) == ops.GQA_ERR_WORKSPACE_TOO_SMALL   # r = 32: the two-launch path checks it too
+    assert call(**{"in": ops.GQA_F32, "d_h": 40, "kn": None}) == ops.GQA_ERR_INVALID_ARGUMENT
+
+    pnames = ["q", "kp", "vp", "kn", "vn", "bt", "wp", "sl", "qp", "o", "B", "h_q", "h_kv", "page", "n_pages",
+              "max_pages", "d_h", "msl", "scale", "in", "out", "ws", "wsb", "stream"]
+    pbase = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 8, 2, 64, 10, 500, 128, 0, 0.088,
+             ops.GQA_BF16, ops.GQA_F32, FAKE, 1 << 30, None]
+
+    def pcall(**kw):
+        a = list(pbase)
+        for k, v in kw.items():
+            a[pnames.index(k)] = v
+        return lib.gqa_append_decode_paged(*a)
+
+    assert pcall(kn=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert pcall(wp=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert pcall(bt=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert pcall(page=48) == ops.GQA_ERR_UNSUPPORTED
+    assert pcall(wsb=0) == ops.GQA_ERR_WORKSPACE_TOO_SMALL

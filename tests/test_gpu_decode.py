@@ -194,3 +194,71 @@ def test_append_then_decode_ragged_small():
     want = _oracle_decode({"q": x["q"], "k_cache": k, "v_cache": v, "seq_lens": x["seq_lens"]}, "bf16",
                           q_pos=x["q_pos"])
     check_parity(got, want, mode="bf16", what="append+decode")
+
+
+# ---------------------------------------------------------------- fused append + decode
+def _append_then_decode(x, kn, vn, wp, dt, fused):
+    """One decode step on fresh device copies of the caches: kv_append then decode as two
+    calls, or the fused call.  Returns (o, k_cache, v_cache) on the host, bit for bit."""
+    import torch
+
+    q, kd, vd = to_dev(x["q"], dt), to_dev(x["k_cache"], dt), to_dev(x["v_cache"], dt)
+    knd, vnd, wpd, sl = to_dev(kn, dt), to_dev(vn, dt), ints_dev(wp), ints_dev(x["seq_lens"])
+    if fused:
+        o = ops.gqa_append_decode(q, kd, vd, knd, vnd, wpd, sl)
+    else:
+        ops.gqa_kv_append(kd, vd, knd, vnd, wpd)
+        o = ops.gqa_decode(q, kd, vd, sl)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.cpu().view(torch.int16).numpy()) if dt == "bf16" else (lambda t: t.cpu().view(torch.int32).numpy())
+    return o.cpu().numpy(), bits(kd), bits(vd)
+
+
+APPEND_CASES = [
+    # dtype, B, h_q, h_kv, T_cap, d_h, seq_lens, write_pos
+    ("bf16", 6, 16, 2, 2048, 128, [1000, 64, 65, 1, 2048, 700], [999, 63, 64, 0, 2047, 699]),   # the usual step
+    ("bf16", 5, 16, 2, 2048, 128, [1000, 64, 500, 300, 9], [1005, -1, 2048, 127, 8]),   # invisible, skipped rows
+    ("bf16", 3, 8, 8, 3000, 64, [3000, 1500, 2], [2999, 1499, 1]),      # MHA, d_h 64
+    ("bf16", 3, 64, 2, 1500, 128, [1500, 700, 3], [1499, 699, 2]),      # r = 32: append and decode launched apart
+    ("f32", 3, 8, 2, 300, 40, [300, 151, 1], [299, 150, 0]),            # fp32 path
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=lambda c: "%s_B%d_hq%d_hkv%d_T%d_d%d" % c[:6])
+def test_append_decode_equals_two_calls(case):
+    """The fused call leaves the same caches and writes the same output, bit for bit, as
+    kv_append followed by decode: rows at and across tile edges, a write position past the
+    visible keys (written, never read), positions outside the cache (skipped), and the
+    shapes that keep two launches."""
+    dt, B, h_q, h_kv, T_cap, d, lens, wp = case
+    print(f"case append+decode {case[:6]}", flush=True)
+    x = inputs.make_decode(B, h_q, h_kv, d, T_cap, dt, 12500 + T_cap, seq_lens=lens, poison=True)
+    kn = inputs.normal(12500 + T_cap, "k_new", (B, h_kv, 1, d), dt)
+    vn = inputs.normal(12500 + T_cap, "v_new", (B, h_kv, 1, d), dt)
+    o2, k2, v2 = _append_then_decode(x, kn, vn, np.array(wp, np.int32), dt, fused=False)
+    o1, k1, v1 = _append_then_decode(x, kn, vn, np.array(wp, np.int32), dt, fused=True)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    assert np.array_equal(o1, o2, equal_nan=True)
+
+
+def test_append_decode_ragged_parity():
+    """Fused step on a ragged batch against the oracle over the appended caches."""
+    import torch
+
+    B, h_q, h_kv, d = 8, 32, 4, 128
+    T_cap = inputs.round_up(3000 + 1, 64)
+    x = inputs.make_append_decode(B, h_q, h_kv, d, T_cap, "bf16", 12600, hist_hi=3000)
+    kd, vd = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+    o = ops.gqa_append_decode(to_dev(x["q"], "bf16"), kd, vd, to_dev(x["k_new"], "bf16"),
+                              to_dev(x["v_new"], "bf16"), ints_dev(x["write_pos"]), ints_dev(x["seq_lens"]),
+                              q_pos=ints_dev(x["q_pos"]), max_seq_len=int(x["seq_lens"].max()))
+    torch.cuda.synchronize()
+    k = x["k_cache"].copy()
+    v = x["v_cache"].copy()
+    for b in range(B):
+        k[b, :, x["hist"][b]] = x["k_new"][b, :, 0]
+        v[b, :, x["hist"][b]] = x["v_new"][b, :, 0]
+    want = _oracle_decode({"q": x["q"], "k_cache": k, "v_cache": v, "seq_lens": x["seq_lens"]}, "bf16",
+                          q_pos=x["q_pos"])
+    check_parity(to_host64(o), want, mode="bf16", what="fused append+decode")
+    assert np.array_equal(kd.cpu().view(torch.int16).numpy(), k.view(np.int16))

@@ -211,3 +211,37 @@ def test_ragged_append_decode_B32_paged_fullsize():
         want = oracle.attention(f64(x["q"][b:b + 1], "bf16"), f64(k, "bf16"), f64(v, "bf16"), causal=True,
                                 q_pos=np.array([[hist[b]]]), kv_len=np.array([L]))
         check_parity(got[b:b + 1], want, mode="bf16", what=f"paged ragged b={b}")
+
+
+@pytest.mark.parametrize("h_q,h_kv,ps", [(16, 2, 64), (16, 4, 128), (64, 2, 64)], ids=["narrow", "narrow_p128", "wide"])
+def test_append_decode_paged_equals_two_calls(h_q, h_kv, ps):
+    """Fused paged step against kv_append_paged + decode_paged on the same pools: the
+    same pools and the same output bit for bit, with one sequence's write position on
+    a missing page (append skipped, row invisible) and one past its visible keys."""
+    import torch
+
+    B, d, mp = 4, 128, 20
+    lens = [ps * mp, ps * 7 + 1, 300, ps]
+    wp = np.array([ps * mp - 1, ps * 7, 310, ps - 1], np.int32)
+    x = inputs.make_decode(B, h_q, h_kv, d, ps * mp, "bf16", 20400 + ps + h_q, seq_lens=lens, poison=True)
+    kn = inputs.normal(20400 + ps, "k_new", (B, h_kv, 1, d), "bf16")
+    vn = inputs.normal(20400 + ps, "v_new", (B, h_kv, 1, d), "bf16")
+    kp, bt = _paginate(x["k_cache"], ps, 17)
+    vp, _ = _paginate(x["v_cache"], ps, 17)
+    bt[1, 7] = -1                              # sequence 1 appends onto a missing page
+    print(f"case paged append+decode h_q={h_q} h_kv={h_kv} page={ps}", flush=True)
+    runs = []
+    for fused in (False, True):
+        q, kpd, vpd = to_dev(x["q"], "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16")
+        knd, vnd, btd, wpd, sl = to_dev(kn, "bf16"), to_dev(vn, "bf16"), ints_dev(bt), ints_dev(wp), ints_dev(lens)
+        if fused:
+            o = ops.gqa_append_decode_paged(q, kpd, vpd, knd, vnd, btd, wpd, sl)
+        else:
+            ops.gqa_kv_append_paged(kpd, vpd, knd, vnd, btd, wpd)
+            o = ops.gqa_decode_paged(q, kpd, vpd, btd, sl)
+        torch.cuda.synchronize()
+        runs.append((o.cpu().numpy(), kpd.cpu().view(torch.int16).numpy(), vpd.cpu().view(torch.int16).numpy()))
+    (o2, k2, v2), (o1, k1, v1) = runs
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    assert np.array_equal(o1, o2)
+    assert np.all(np.isfinite(o1))
