@@ -67,16 +67,23 @@ def test_decode_sweep_sampled(name):
     _decode_sampled(inputs.WORKLOADS[name], [0, 7])
 
 
-def test_ragged_append_decode_B32_sampled():
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
+def test_ragged_append_decode_B32_sampled(fused):
+    """The ragged step as kv_append then decode, and as the one fused call the
+    benchmark times."""
     import torch
 
     w = inputs.WORKLOADS["ragged_append_decode_B32"]
-    print(f"case {w.name}", flush=True)
+    print(f"case {w.name} fused={fused}", flush=True)
     x = inputs.make_workload(w)
     kd, vd = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
-    ops.gqa_kv_append(kd, vd, to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints_dev(x["write_pos"]))
-    o = ops.gqa_decode(to_dev(x["q"], "bf16"), kd, vd, ints_dev(x["seq_lens"]), q_pos=ints_dev(x["q_pos"]),
-                       max_seq_len=int(x["seq_lens"].max()))
+    kn, vn, wp = to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints_dev(x["write_pos"])
+    q, sl, qp, msl = to_dev(x["q"], "bf16"), ints_dev(x["seq_lens"]), ints_dev(x["q_pos"]), int(x["seq_lens"].max())
+    if fused:
+        o = ops.gqa_append_decode(q, kd, vd, kn, vn, wp, sl, q_pos=qp, max_seq_len=msl)
+    else:
+        ops.gqa_kv_append(kd, vd, kn, vn, wp)
+        o = ops.gqa_decode(q, kd, vd, sl, q_pos=qp, max_seq_len=msl)
     torch.cuda.synchronize()
     got = to_host64(o)
     assert np.all(np.isfinite(got))

@@ -191,16 +191,23 @@ def test_ragged_append_decode_B32_paged_fullsize():
         return pool
 
     kp, vp = pool_of(kd), pool_of(vd)
+    kp2, vp2 = pool_of(kd), pool_of(vd)
     btd = perm.view(w.B, mp).to(torch.int32).contiguous()
     kn, vn, wp = to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16"), ints_dev(x["write_pos"])
     lens, qp, msl = ints_dev(x["seq_lens"]), ints_dev(x["q_pos"]), int(x["seq_lens"].max())
+    q = to_dev(x["q"], "bf16")
     ops.gqa_kv_append_paged(kp, vp, kn, vn, btd, wp)
-    got_p = ops.gqa_decode_paged(to_dev(x["q"], "bf16"), kp, vp, btd, lens, q_pos=qp, max_seq_len=msl)
+    got_p = ops.gqa_decode_paged(q, kp, vp, btd, lens, q_pos=qp, max_seq_len=msl)
+    # the fused call the benchmark times, on a second copy of the pools
+    got_f = ops.gqa_append_decode_paged(q, kp2, vp2, kn, vn, btd, wp, lens, q_pos=qp, max_seq_len=msl)
     ops.gqa_kv_append(kd, vd, kn, vn, wp)
-    got_c = ops.gqa_decode(to_dev(x["q"], "bf16"), kd, vd, lens, q_pos=qp, max_seq_len=msl)
+    got_c = ops.gqa_decode(q, kd, vd, lens, q_pos=qp, max_seq_len=msl)
     torch.cuda.synchronize()
     got = to_host64(got_p)
     assert np.array_equal(got, to_host64(got_c))
+    assert np.array_equal(got, to_host64(got_f))
+    assert torch.equal(kp.view(torch.int16), kp2.view(torch.int16)) and torch.equal(vp.view(torch.int16), vp2.view(torch.int16))
+    del kp2, vp2
     hist = x["hist"]
     for b in sorted({int(np.argmin(hist)), int(np.argmax(hist)), 9}):
         L = int(x["seq_lens"][b])
