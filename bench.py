@@ -326,11 +326,22 @@ def bench_rope(steps, warmup, flush_buf):
     ms = sum(per) / len(per)
     nbytes = 2 * (q.numel() + k.numel()) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
+    # the prefill with Q rotated inside the kernel, against gqa_rope on Q then the prefill
+    v = torch.randn((w.B, w.h_kv, w.T, w.d_h), device="cuda").to(torch.bfloat16)
+    out = torch.empty((w.B, w.h_q, w.T, w.d_h), dtype=torch.float32, device="cuda")
+    flops = 4 * w.B * w.h_q * w.d_h * (w.T * (w.T + 1) // 2)
+    log(f"[bench] timing {w.name} with Q rotated inside the prefill kernel, and rotated beforehand")
+    _, fused_ms = time_region(lambda: ops.gqa_prefill_rope(q, ko, v, out=out), steps, warmup)
+    _, sep_ms = time_region(lambda: (ops.gqa_rope(q, out=qo), ops.gqa_prefill(qo, ko, v, out=out)), steps, warmup)
+    del v, out
     return {"workload": w.name + "_qk_rope", "rows": w.B * (w.h_q + w.h_kv) * w.T, "d_h": w.d_h,
             "algorithmic_bytes": nbytes, "ms_per_call": round(ms, 5), "value": round(gbs, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
-            "kernels": "rope (Q) + rope (K)"}
+            "kernels": "rope (Q) + rope (K)",
+            "prefill_rope_fused": {"ms_per_call": round(fused_ms, 5),
+                                   "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+                                   "rope_then_prefill_ms": round(sep_ms, 5)}}
 
 
 # ---------------------------------------------------------------------------------------- CPU oracle

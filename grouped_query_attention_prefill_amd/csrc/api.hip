@@ -90,7 +90,7 @@ int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
 
 static int prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int h_q, int h_kv, int T, int d_h, int mask, const int32_t* kv_lens, float scale,
-                        int in_dtype, int out_dtype, void* stream) {
+                        int in_dtype, int out_dtype, void* stream, float rope_base = 0.f) {
   if (B < 1 || h_q < 1 || h_kv < 1 || T < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (mask != GQA_MASK_NONE && mask != GQA_MASK_CAUSAL) return GQA_ERR_INVALID_ARGUMENT;
@@ -112,6 +112,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   a.scale = scale;
   a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
   a.lse = lse;
+  a.rope_base = rope_base;
   return run_attention(a, in_dtype, stream);
 }
 
@@ -120,6 +121,16 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o,
                 int mask, const int32_t* kv_lens, float scale,
                 int in_dtype, int out_dtype, void* stream) {
   return prefill_impl(q, k, v, o, nullptr, B, h_q, h_kv, T, d_h, mask, kv_lens, scale, in_dtype, out_dtype, stream);
+}
+
+int gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
+                     int B, int h_q, int h_kv, int T, int d_h,
+                     int mask, const int32_t* kv_lens, float scale, float rope_base,
+                     int in_dtype, int out_dtype, void* stream) {
+  if (!std::isfinite(rope_base) || rope_base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  if (known_dtype(in_dtype) && in_dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  return prefill_impl(q, k, v, o, nullptr, B, h_q, h_kv, T, d_h, mask, kv_lens, scale, in_dtype, out_dtype, stream,
+                      rope_base);
 }
 
 int gqa_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -195,7 +206,8 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* seq_lens, const int32_t* q_pos, void* o,
                        int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
                        float scale, int in_dtype, int out_dtype,
-                       void* workspace, size_t workspace_bytes, void* stream, const AppendIn* ap) {
+                       void* workspace, size_t workspace_bytes, void* stream, const AppendIn* ap,
+                       float rope_base = 0.f) {
   if (B < 1 || h_q < 1 || h_kv < 1 || T_cap < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (max_seq_len > T_cap) return GQA_ERR_INVALID_ARGUMENT;
@@ -208,8 +220,10 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (!seq_lens || !aligned(seq_lens, 4) || (q_pos && !aligned(q_pos, 4))) return GQA_ERR_INVALID_ARGUMENT;
   const int eb = in_dtype == GQA_BF16 ? 2 : 4;
   if (ap && !append_ptrs_ok(*ap, k_cache, v_cache, d_h, eb)) return GQA_ERR_INVALID_ARGUMENT;
+  if (rope_base != 0.f && in_dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
   const int len = max_seq_len > 0 ? max_seq_len : T_cap;
   DecodeArgs a;
+  a.rope_base = rope_base;
   a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.q_pos = q_pos; a.o = o;
   a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.T_cap = T_cap; a.D = d_h; a.max_len = len;
   a.scale = scale;
@@ -226,8 +240,12 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   }
   const bool fused = ap && in_dtype == GQA_BF16 && h_q / h_kv <= 16;
   if (ap && !fused) {
-    const hipError_t e = gqa::launch_kv_append(const_cast<void*>(k_cache), const_cast<void*>(v_cache), ap->k_new,
-                                               ap->v_new, ap->write_pos, B, h_kv, T_cap, d_h, eb, s);
+    const hipError_t e =
+        rope_base != 0.f
+            ? gqa::launch_kv_append_rope(const_cast<void*>(k_cache), const_cast<void*>(v_cache), ap->k_new,
+                                         ap->v_new, ap->write_pos, B, h_kv, T_cap, d_h, rope_base, eb, s)
+            : gqa::launch_kv_append(const_cast<void*>(k_cache), const_cast<void*>(v_cache), ap->k_new, ap->v_new,
+                                    ap->write_pos, B, h_kv, T_cap, d_h, eb, s);
     if (e != hipSuccess) return GQA_ERR_HIP;
   }
   if (fused) { a.k_new = ap->k_new; a.v_new = ap->v_new; a.write_pos = ap->write_pos; }
@@ -300,6 +318,17 @@ int gqa_append_decode(const void* q, void* k_cache, void* v_cache, const void* k
   const AppendIn ap{k_new, v_new, write_pos};
   return decode_impl(q, k_cache, v_cache, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, max_seq_len, scale,
                      in_dtype, out_dtype, workspace, workspace_bytes, stream, &ap);
+}
+
+int gqa_append_decode_rope(const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int32_t* write_pos, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                           int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+                           float scale, float rope_base, int in_dtype, int out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!std::isfinite(rope_base) || rope_base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  const AppendIn ap{k_new, v_new, write_pos};
+  return decode_impl(q, k_cache, v_cache, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, max_seq_len, scale,
+                     in_dtype, out_dtype, workspace, workspace_bytes, stream, &ap, rope_base);
 }
 
 int gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -21,6 +21,7 @@
 // requests in flight; larger groups use 32x32 tiles over 128-key tiles.
 #include "internal.h"
 #include "mfma_common.h"
+#include "rope_common.h"
 
 namespace gqa {
 namespace {
@@ -57,7 +58,35 @@ struct DecodeParams {
   const uint16_t* v_new;
   const int32_t* write_pos;
   float c;            // scale * log2(e)
+  int rope;           // the ROPE kernels: Q (and the appended key) rotated as loaded
+  RopeTheta rope_theta;
 };
+
+// Position of sequence b's query (rotary encoding of Q): q_pos[b], else its last row.
+__device__ __forceinline__ int query_position(const DecodeParams& p, int b) {
+  return p.q_pos ? p.q_pos[b] : clampi(p.seq_lens[b], 0, p.T_cap) - 1;
+}
+
+// Elements 8 c8 .. 8 c8 + 7 of the key row appended to (b, g), rotated at position
+// wp in the ROPE kernels (each 16-byte chunk also reads its partner chunk, d/2 away).
+template <int D, bool ROPE>
+__device__ __forceinline__ uint4 new_key_chunk(const DecodeParams& p, int b, int g, int c8, int wp) {
+  const uint16_t* src = p.k_new + (size_t)(b * p.h_kv + g) * D;
+  uint4 x = *reinterpret_cast<const uint4*>(src + c8 * 8);
+  if constexpr (ROPE) {
+    constexpr int HC = D / 16;                 // 16-byte chunks per half row
+    const bool lo = c8 < HC;
+    const uint4 y = *reinterpret_cast<const uint4*>(src + (lo ? c8 + HC : c8 - HC) * 8);
+    bf16x8 a = __builtin_bit_cast(bf16x8, lo ? x : y), u = __builtin_bit_cast(bf16x8, lo ? y : x);
+    const int i0 = (lo ? c8 : c8 - HC) * 8;
+    double th[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) th[e] = p.rope_theta.t[i0 + e];
+    rope_rotate8(a, u, wp, th);
+    x = __builtin_bit_cast(uint4, lo ? a : u);
+  }
+  return x;
+}
 
 template <int D>
 struct DecodeLds {
@@ -126,7 +155,7 @@ __device__ __forceinline__ KvSpan kv_span(const DecodeParams& p, int b, int g, i
   return KvSpan{p.k + off, p.v + off, valid};
 }
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, bool ROPE>
 __global__ void __launch_bounds__(kThreads, 2)
 decode_bf16_kernel(DecodeParams p) {
   using L = DecodeLds<D>;
@@ -175,6 +204,17 @@ decode_bf16_kernel(DecodeParams p) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (col_valid) x = *reinterpret_cast<const uint4*>(qrow + ks * 16 + h * 8);
       qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+    if constexpr (ROPE) {
+      // qf[ks] and qf[ks + D/32] hold elements 16 ks + 8 h + e and their partners
+      const int qp = query_position(p, b);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        double th[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) th[e] = h ? p.rope_theta.t[16 * ks + 8 + e] : p.rope_theta.t[16 * ks + e];
+        rope_rotate8(qf[ks], qf[ks + D / 32], qp, th);
+      }
     }
   }
 
@@ -390,7 +430,7 @@ struct Decode16Lds {
   static constexpr int TOTAL = STAGE > MERGE ? STAGE : MERGE;
 };
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, bool ROPE>
 __global__ void __launch_bounds__(kThreads, 4)
 decode16_bf16_kernel(DecodeParams p) {
   using L = Decode16Lds<D>;
@@ -442,8 +482,7 @@ decode16_bf16_kernel(DecodeParams p) {
         const size_t src = (size_t)(b * p.h_kv + g) * D + c8 * 8;
         // the caches are the caller's writable buffers; only this path writes them
         if (tid < D / 8)
-          *reinterpret_cast<uint4*>(const_cast<uint16_t*>(p.k) + row + c8 * 8) =
-              *reinterpret_cast<const uint4*>(p.k_new + src);
+          *reinterpret_cast<uint4*>(const_cast<uint16_t*>(p.k) + row + c8 * 8) = new_key_chunk<D, ROPE>(p, b, g, c8, wp);
         else
           *reinterpret_cast<uint4*>(const_cast<uint16_t*>(p.v) + row + c8 * 8) =
               *reinterpret_cast<const uint4*>(p.v_new + src);
@@ -472,6 +511,20 @@ decode16_bf16_kernel(DecodeParams p) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (q_valid) x = *reinterpret_cast<const uint4*>(qrow + kd * 32 + G * 8);
       qf[kd] = __builtin_bit_cast(bf16x8, x);
+    }
+    if constexpr (ROPE) {
+      // qf[kd] and qf[kd + D/64] hold elements 32 kd + 8 G + e and their partners
+      const int qp = query_position(p, b);
+#pragma unroll
+      for (int kd = 0; kd < D / 64; ++kd) {
+        double th[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double* t = p.rope_theta.t + 32 * kd + e;
+          th[e] = G == 0 ? t[0] : G == 1 ? t[8] : G == 2 ? t[16] : t[24];
+        }
+        rope_rotate8(qf[kd], qf[kd + D / 64], qp, th);
+      }
     }
   }
 
@@ -505,9 +558,8 @@ decode16_bf16_kernel(DecodeParams p) {
         const int u = tid + kThreads * i;
         const int row = u / (D / 8), c8 = u % (D / 8);
         if (k0 + row == wp) {
-          const size_t src = (size_t)(b * p.h_kv + g) * D + c8 * 8;
-          kreg[i] = *reinterpret_cast<const uint4*>(p.k_new + src);
-          vreg[i] = *reinterpret_cast<const uint4*>(p.v_new + src);
+          kreg[i] = new_key_chunk<D, ROPE>(p, b, g, c8, wp);
+          vreg[i] = *reinterpret_cast<const uint4*>(p.v_new + (size_t)(b * p.h_kv + g) * D + c8 * 8);
         }
       }
     }
@@ -763,26 +815,31 @@ decode_combine_many_kernel(DecodeParams p) {
   }
 }
 
-template <int D, bool OUT_BF16>
-hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
+template <int D, bool OUT_BF16, bool ROPE>
+hipError_t launch_split(const DecodeParams& prm, int B, hipStream_t s) {
   if (prm.r <= 16) {
     constexpr int smem = Decode16Lds<D>::TOTAL;
     static std::atomic<unsigned long long> lds_allowed{0};
-    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(decode16_bf16_kernel<D, OUT_BF16>), smem,
-                                           lds_allowed);
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(decode16_bf16_kernel<D, OUT_BF16, ROPE>),
+                                           smem, lds_allowed);
     if (e != hipSuccess) return e;
     dim3 grid(prm.n_split, prm.h_kv, B);
-    hipLaunchKernelGGL((decode16_bf16_kernel<D, OUT_BF16>), grid, dim3(kThreads), smem, s, prm);
+    hipLaunchKernelGGL((decode16_bf16_kernel<D, OUT_BF16, ROPE>), grid, dim3(kThreads), smem, s, prm);
   } else {
     constexpr int smem = DecodeLds<D>::TOTAL;
     static std::atomic<unsigned long long> lds_allowed{0};
-    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(decode_bf16_kernel<D, OUT_BF16>), smem,
-                                           lds_allowed);
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(decode_bf16_kernel<D, OUT_BF16, ROPE>),
+                                           smem, lds_allowed);
     if (e != hipSuccess) return e;
     dim3 grid(prm.n_split, prm.h_kv * prm.hc_count, B);
-    hipLaunchKernelGGL((decode_bf16_kernel<D, OUT_BF16>), grid, dim3(kThreads), smem, s, prm);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, OUT_BF16, ROPE>), grid, dim3(kThreads), smem, s, prm);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <int D, bool OUT_BF16>
+hipError_t launch_t(const DecodeParams& prm, int B, hipStream_t s) {
+  hipError_t e = prm.rope ? launch_split<D, OUT_BF16, true>(prm, B, s) : launch_split<D, OUT_BF16, false>(prm, B, s);
   if (e != hipSuccess || prm.direct) return e;
   if (prm.n_split > kManySplits)
     hipLaunchKernelGGL((decode_combine_many_kernel<D, OUT_BF16>), dim3(prm.h_q, B), dim3(256), 0, s, prm);
@@ -845,6 +902,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& pl, hipStre
   p.v_new = static_cast<const uint16_t*>(a.v_new);
   p.write_pos = a.write_pos;
   p.c = a.scale * kLog2e;
+  p.rope = a.rope_base > 0.f ? 1 : 0;
+  p.rope_theta = p.rope ? make_rope_theta(a.D, a.rope_base) : RopeTheta{};
   const size_t u_bytes = (size_t)a.B * a.h_q * pl.n_split_cap * a.D * sizeof(float);
   p.ws_u = static_cast<float*>(a.workspace);
   p.ws_ml = a.workspace ? reinterpret_cast<float*>(static_cast<char*>(a.workspace) + u_bytes) : nullptr;

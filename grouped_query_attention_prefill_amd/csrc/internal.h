@@ -40,6 +40,7 @@ struct AttnArgs {
   float scale;
   int out_bf16;           // output dtype of the bf16 path
   float* lse = nullptr;   // (B, h_q, S_q) natural-log row log-sum-exp of the scaled scores, or null
+  float rope_base = 0.f;  // > 0: Q rotated at each row's position as it is loaded (bf16 path)
 };
 
 // Decode: one query per sequence at q_pos[b] (null -> seq_lens[b] - 1), keys
@@ -65,6 +66,9 @@ struct DecodeArgs {
   const void* k_new = nullptr;
   const void* v_new = nullptr;
   const int32_t* write_pos = nullptr;
+  // > 0: rotary encoding inside the kernels, Q at its query position and (fused
+  // append) the new key at write_pos[b]
+  float rope_base = 0.f;
 };
 
 struct DecodePlan {

@@ -45,6 +45,7 @@
 
 #include "internal.h"
 #include "mfma_common.h"
+#include "rope_common.h"
 
 namespace gqa {
 namespace {
@@ -69,6 +70,8 @@ struct PrefillParams {
   int xcd_remap;
   float c;                      // scale * log2(e)
   float scale;
+  int rope;                     // rotate Q at each row's position as it is loaded (the ROPE kernels)
+  RopeTheta rope_theta;
 };
 
 template <int D>
@@ -81,7 +84,7 @@ struct PrefillLds {
   static constexpr int TOTAL = 2 * K_STAGE + 2 * V_STAGE;
 };
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, bool ROPE>
 __global__ void __launch_bounds__(kThreads, 1)
 prefill_bf16_kernel(PrefillParams p) {
   using L = PrefillLds<D>;
@@ -125,8 +128,8 @@ prefill_bf16_kernel(PrefillParams p) {
   const int n_tiles = (kv_end + kTile - 1) / kTile;
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
-  bf16x8 qf[D / 16];
-  {
+  bf16x8 qf[D / 16] = {};
+  if constexpr (!ROPE) {
     const uint16_t* qrow = p.q + ((size_t)(b * p.h_q + head) * p.S_q + qi) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -135,6 +138,52 @@ prefill_bf16_kernel(PrefillParams p) {
       qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  // Rotary encoding at each row's absolute position, applied to the workgroup's Q
+  // rows staged in LDS (free until the first tile is stored): wave w turns the pairs
+  // 8 w .. 8 w + 7 of rows lane + 64 k, so its angles are wave-uniform; then every
+  // lane reads its fragments as above.  Called once the first tile's loads are in
+  // flight, so their latency covers this work.
+  auto load_q_rotated = [&]() {
+    constexpr int QS = D * 2 + 16;                       // row stride, bytes (<= the K/V stages)
+    constexpr int CH = D / 8;                            // 16-byte chunks per row
+    static_assert(kRowsWG * QS <= PrefillLds<D>::TOTAL, "Q rows fit the stage space");
+#pragma unroll
+    for (int j = 0; j < kRowsWG * CH / kThreads; ++j) {
+      const int u = tid + kThreads * j;
+      const int r_ = u / CH, c_ = u % CH;
+      const int hh_ = hc * p.hp + r_ / p.P, qi_ = qb * p.P + r_ % p.P;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (qi_ < p.S_q)
+        x = *reinterpret_cast<const uint4*>(p.q + ((size_t)(b * p.h_q + g * p.r + hh_) * p.S_q + qi_) * D + c_ * 8);
+      *reinterpret_cast<uint4*>(lds + r_ * QS + c_ * 16) = x;
+    }
+    lds_barrier();
+    constexpr int PAIR_CH = D / 16;                      // 8-pair chunks per row
+#pragma unroll
+    for (int cc = 0; cc < PAIR_CH; cc += kThreads / 64) {
+      const int c_ = cc + wave;                          // wave-uniform
+      if (c_ < PAIR_CH) {
+        double th[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) th[e] = p.rope_theta.t[8 * c_ + e];
+#pragma unroll
+        for (int k_ = 0; k_ < kRowsWG / 64; ++k_) {
+          const int r_ = lane + 64 * k_;
+          unsigned char* rowp = lds + r_ * QS;
+          bf16x8 lo = *reinterpret_cast<const bf16x8*>(rowp + c_ * 16);
+          bf16x8 hi = *reinterpret_cast<const bf16x8*>(rowp + (c_ + PAIR_CH) * 16);
+          rope_rotate8(lo, hi, pos0 + qb * p.P + r_ % p.P, th);
+          *reinterpret_cast<bf16x8*>(rowp + c_ * 16) = lo;
+          *reinterpret_cast<bf16x8*>(rowp + (c_ + PAIR_CH) * 16) = hi;
+        }
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(lds + rho * QS + (ks * 16 + h * 8) * 2);
+    lds_barrier();                                     // the stages may be written from here on
+  };
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -317,6 +366,7 @@ prefill_bf16_kernel(PrefillParams p) {
     const auto yes = std::integral_constant<bool, true>{};
     const auto no = std::integral_constant<bool, false>{};
     load_tile(0);
+    if constexpr (ROPE) load_q_rotated();
     if (grp == 0) {
       store_tile(0);
       if (n_tiles > 1) load_tile(1);
@@ -369,15 +419,20 @@ prefill_bf16_kernel(PrefillParams p) {
   }
 }
 
-template <int D, bool OUT_BF16>
-hipError_t launch_t(const PrefillParams& prm, int total, hipStream_t s) {
+template <int D, bool OUT_BF16, bool ROPE>
+hipError_t launch_v(const PrefillParams& prm, int total, hipStream_t s) {
   constexpr int smem = PrefillLds<D>::TOTAL;
   static std::atomic<unsigned long long> lds_allowed{0};
-  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(prefill_bf16_kernel<D, OUT_BF16>), smem,
-                                         lds_allowed);
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(prefill_bf16_kernel<D, OUT_BF16, ROPE>),
+                                         smem, lds_allowed);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16>), dim3(total), dim3(kThreads), smem, s, prm);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, ROPE>), dim3(total), dim3(kThreads), smem, s, prm);
   return hipGetLastError();
+}
+
+template <int D, bool OUT_BF16>
+hipError_t launch_t(const PrefillParams& prm, int total, hipStream_t s) {
+  return prm.rope ? launch_v<D, OUT_BF16, true>(prm, total, s) : launch_v<D, OUT_BF16, false>(prm, total, s);
 }
 
 }  // namespace
@@ -403,6 +458,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   p.n_hchunks = p.r / hp;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
+  p.rope = a.rope_base > 0.f ? 1 : 0;
+  p.rope_theta = p.rope ? make_rope_theta(a.D, a.rope_base) : RopeTheta{};
   const long long total = (long long)a.B * a.h_kv * p.n_hchunks * p.n_qblocks;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;

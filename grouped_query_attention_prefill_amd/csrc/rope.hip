@@ -8,40 +8,20 @@
 // reads it; and the rotation is applied to the new key on its way into the cache,
 // never to rows already stored, which other readers may share ([Ch09] 09.4).
 //
-// The pages print no rotation formula; the form used is the common one, pair
-// (x[i], x[i + d/2]) turned by the angle p * theta_i, theta_i = base^(-2 i / d):
-//     y[i]       = x[i] cos - x[i + d/2] sin,   y[i + d/2] = x[i + d/2] cos + x[i] sin.
-// theta_i comes from the host in double precision, the angle p * theta_i is formed
-// and reduced to a fraction of a turn in double precision (angles reach 3e4
-// radians at the lengths served), and the hardware sine and cosine (which take
-// turns) are applied to that fraction in single precision.  Elements are read and
-// written in the tensor's own precision; the arithmetic is fp32.
+// The rotation (pair (x[i], x[i + d/2]) turned by p * base^(-2 i / d), angles
+// reduced to turns in double precision, hardware sine and cosine) is in
+// rope_common.h, shared with the attention kernels that rotate Q as they load it.
+// Elements are read and written in the tensor's own precision; the arithmetic is fp32.
 #include "internal.h"
+#include "rope_common.h"
 
 namespace gqa {
 namespace {
 
-struct RopeFreq {
-  double inv_freq[kRopeMaxHalf];   // theta_i, i < d / 2
-};
-
 __device__ __forceinline__ float ld(const float* p) { return *p; }
-__device__ __forceinline__ float ld(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float ld(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 __device__ __forceinline__ void st(float* p, float v) { *p = v; }
-__device__ __forceinline__ void st(uint16_t* p, float v) {
-  const __bf16 b = (__bf16)v;                  // round to nearest even
-  *p = __builtin_bit_cast(uint16_t, b);
-}
-
-// cos and sin of p * theta: the angle is reduced in double precision to a fraction
-// of a turn in [-1/2, 1/2]; the hardware sine and cosine take that fraction.
-__device__ __forceinline__ void rot_cos_sin(int p, double theta, float& c, float& s) {
-  constexpr double kInv2Pi = 0.15915494309189533577;
-  const double turns = (double)p * theta * kInv2Pi;
-  const float f = (float)(turns - rint(turns));
-  c = __builtin_amdgcn_cosf(f);
-  s = __builtin_amdgcn_sinf(f);
-}
+__device__ __forceinline__ void st(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
 
 template <typename T, int VEC>
 struct Vec;
@@ -75,11 +55,11 @@ rope_kernel(const T* x, T* y, const int32_t* pos0, int H, int S, int half, long 
   T* u = reinterpret_cast<T*>(&hi);
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
-    float c, sn;
-    rot_cos_sin(p, f.inv_freq[i0 + v], c, sn);
-    const float x0 = ld(l + v), x1 = ld(u + v);
-    st(l + v, x0 * c - x1 * sn);
-    st(u + v, x1 * c + x0 * sn);
+    float c, sn, y0, y1;
+    rope_cos_sin(p, f.inv_freq[i0 + v], c, sn);
+    rope_rotate(ld(l + v), ld(u + v), c, sn, y0, y1);
+    st(l + v, y0);
+    st(u + v, y1);
   }
   *reinterpret_cast<V*>(yr) = lo;
   *reinterpret_cast<V*>(yr + half) = hi;
@@ -101,21 +81,13 @@ kv_append_rope_kernel(T* kc, T* vc, const T* kn, const T* vn, const int32_t* wri
   T* kd = kc + ((size_t)(b * h_kv + g) * T_cap + wp) * d;
   T* vd = vc + ((size_t)(b * h_kv + g) * T_cap + wp) * d;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    float c, sn;
-    rot_cos_sin(wp, f.inv_freq[i], c, sn);
-    const float x0 = ld(ks + i), x1 = ld(ks + i + half);
-    st(kd + i, x0 * c - x1 * sn);
-    st(kd + i + half, x1 * c + x0 * sn);
+    float c, sn, y0, y1;
+    rope_cos_sin(wp, f.inv_freq[i], c, sn);
+    rope_rotate(ld(ks + i), ld(ks + i + half), c, sn, y0, y1);
+    st(kd + i, y0);
+    st(kd + i + half, y1);
   }
   for (int i = threadIdx.x; i < d; i += blockDim.x) vd[i] = vs[i];
-}
-
-RopeFreq make_freq(int d, float base) {
-  RopeFreq f;
-  const int half = d / 2;
-  for (int i = 0; i < kRopeMaxHalf; ++i)
-    f.inv_freq[i] = i < half ? std::pow((double)base, -2.0 * i / d) : 0.0;
-  return f;
 }
 
 }  // namespace
@@ -124,7 +96,7 @@ hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H
                        float base, int elem_bytes, hipStream_t s) {
   const int half = D / 2;
   const long long n_rows = (long long)B * H * S;
-  const RopeFreq f = make_freq(D, base);
+  const RopeFreq f = make_rope_freq(D, base);
   const bool al16 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
   const int vec = !al16 ? 1 : (elem_bytes == 4 ? (half % 4 == 0 ? 4 : 1) : (half % 8 == 0 ? 8 : 1));
   const long long n_chunks = n_rows * (half / vec);
@@ -148,7 +120,7 @@ hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H
 hipError_t launch_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                                  const int32_t* write_pos, int B, int h_kv, int T_cap, int D, float base,
                                  int elem_bytes, hipStream_t s) {
-  const RopeFreq f = make_freq(D, base);
+  const RopeFreq f = make_rope_freq(D, base);
   if (elem_bytes == 4)
     hipLaunchKernelGGL(kv_append_rope_kernel<float>, dim3(h_kv, B), dim3(128), 0, s,
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), static_cast<const float*>(k_new),

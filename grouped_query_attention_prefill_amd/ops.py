@@ -39,6 +39,9 @@ SIGNATURES = {
     "gqa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "gqa_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gqa_append_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
+    "gqa_prefill_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _F, _I, _I, _P]),
+    "gqa_append_decode_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I,
+                                    _P, _S, _P]),
     "gqa_append_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                      _I, _I, _P, _S, _P]),
     "gqa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
@@ -157,12 +160,7 @@ def _out_code(in_code: int, out_dtype) -> int:
 
 
 # ------------------------------------------------------------------ entry points
-def gqa_prefill(q, k, v, *, causal: bool = True, scale: Optional[float] = None, kv_lens=None,
-                out=None, out_dtype=None):
-    """O = grouped-query attention of q (B,h_q,T,d_h) over k, v (B,h_kv,T,d_h).
-
-    Returns ``out`` (allocated with ``torch.empty`` when None); fp32 output by default.
-    """
+def _prefill_args(q, k, v, kv_lens, out, out_dtype):
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(t, n, 4)
@@ -170,7 +168,6 @@ def gqa_prefill(q, k, v, *, causal: bool = True, scale: Optional[float] = None, 
     _require(k.shape == v.shape and k.shape[0] == B and k.shape[2] == T and k.shape[3] == d_h,
              "k, v must be (B, h_kv, T, d_h) matching q")
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
-    h_kv = k.shape[1]
     code = _dtype_code(q)
     oc = _out_code(code, out_dtype if out is None else out.dtype)
     if out is None:
@@ -178,11 +175,32 @@ def gqa_prefill(q, k, v, *, causal: bool = True, scale: Optional[float] = None, 
     _dev_tensor(out, "out", 4)
     _require(tuple(out.shape) == (B, h_q, T, d_h), "out must be (B, h_q, T, d_h)")
     kv_lens = _int_vec(kv_lens, "kv_lens", B, q.device)
+    return B, h_q, k.shape[1], T, d_h, code, oc, out, kv_lens
+
+
+def gqa_prefill(q, k, v, *, causal: bool = True, scale: Optional[float] = None, kv_lens=None,
+                out=None, out_dtype=None):
+    """O = grouped-query attention of q (B,h_q,T,d_h) over k, v (B,h_kv,T,d_h).
+
+    Returns ``out`` (allocated with ``torch.empty`` when None); fp32 output by default.
+    """
+    B, h_q, h_kv, T, d_h, code, oc, out, kv_lens = _prefill_args(q, k, v, kv_lens, out, out_dtype)
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
-    lib = load_library()
-    _launch(q.device, (("k", k), ("v", v), ("out", out)), lib.gqa_prefill,
+    _launch(q.device, (("k", k), ("v", v), ("out", out)), load_library().gqa_prefill,
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h_q, h_kv, T, d_h,
             GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc, code, oc)
+    return out
+
+
+def gqa_prefill_rope(q, k, v, *, causal: bool = True, scale: Optional[float] = None, kv_lens=None,
+                     base: float = 10000.0, out=None, out_dtype=None):
+    """gqa_prefill with query row i rotated at position i inside the kernel (k must
+    already hold rotated keys); equals gqa_prefill(gqa_rope(q), k, v) bit for bit."""
+    B, h_q, h_kv, T, d_h, code, oc, out, kv_lens = _prefill_args(q, k, v, kv_lens, out, out_dtype)
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    _launch(q.device, (("k", k), ("v", v), ("out", out)), load_library().gqa_prefill_rope,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h_q, h_kv, T, d_h,
+            GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), sc, float(base), code, oc)
     return out
 
 
@@ -283,6 +301,21 @@ def gqa_append_decode(q, k_cache, v_cache, k_new, v_new, write_pos, seq_lens, *,
                       scale: Optional[float] = None, max_seq_len: Optional[int] = None, out=None, out_dtype=None,
                       workspace=None):
     """gqa_kv_append(k_cache, v_cache, k_new, v_new, write_pos) then gqa_decode(...), in one call."""
+    return _append_decode(q, k_cache, v_cache, k_new, v_new, write_pos, seq_lens, q_pos, scale, max_seq_len, out,
+                          out_dtype, workspace, None)
+
+
+def gqa_append_decode_rope(q, k_cache, v_cache, k_new, v_new, write_pos, seq_lens, *, q_pos=None,
+                           scale: Optional[float] = None, max_seq_len: Optional[int] = None, base: float = 10000.0,
+                           out=None, out_dtype=None, workspace=None):
+    """gqa_kv_append_rope (k_new rotated at write_pos) then gqa_decode with each query
+    rotated at its position (q_pos, else seq_lens - 1), in one call."""
+    return _append_decode(q, k_cache, v_cache, k_new, v_new, write_pos, seq_lens, q_pos, scale, max_seq_len, out,
+                          out_dtype, workspace, float(base))
+
+
+def _append_decode(q, k_cache, v_cache, k_new, v_new, write_pos, seq_lens, q_pos, scale, max_seq_len, out,
+                   out_dtype, workspace, rope_base):
     torch = _torch()
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev_tensor(t, n, 4)
@@ -311,10 +344,14 @@ def gqa_append_decode(q, k_cache, v_cache, k_new, v_new, write_pos, seq_lens, *,
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
     msl = 0 if max_seq_len is None else int(max_seq_len)
-    _launch(q.device, (("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("workspace", workspace)),
-            lib.gqa_append_decode, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
-            _ptr(write_pos), _ptr(seq_lens), _ptr(q_pos), _ptr(out), B, h_q, h_kv, T_cap, d_h, msl, sc, code, oc,
-            _ptr(workspace), ws_have)
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(write_pos), _ptr(seq_lens),
+            _ptr(q_pos), _ptr(out), B, h_q, h_kv, T_cap, d_h, msl, sc)
+    tail = (code, oc, _ptr(workspace), ws_have)
+    tensors = (("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("workspace", workspace))
+    if rope_base is None:
+        _launch(q.device, tensors, lib.gqa_append_decode, *head, *tail)
+    else:
+        _launch(q.device, tensors, lib.gqa_append_decode_rope, *head, rope_base, *tail)
     return out
 
 

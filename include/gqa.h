@@ -221,6 +221,40 @@ int gqa_append_decode_paged(const void* q, void* k_pages, void* v_pages, const v
                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Rotary position encoding inside the attention kernels.  Every query head and
+ * every stored key head is rotated by its position before the scores are formed
+ * ([EffSeq] 分组查询注意力; [MhaMqaGqa] note under the parameter table), in the
+ * form gqa_rope applies (pair (x[i], x[i + d_h/2]) turned by
+ * p * rope_base^(-2 i / d_h)).  These calls rotate Q as the kernels load it, so
+ * no rotated copy of Q is written; results are bit-identical to gqa_rope on Q
+ * followed by the plain call.  Keys are not rotated here: K (prefill) or the
+ * cache (decode) must already hold rotated keys, as gqa_rope on the prompt's K
+ * and gqa_kv_append_rope leave them.
+ *
+ * gqa_prefill_rope: gqa_prefill with query row i rotated at position i.
+ * Supported: in_dtype GQA_BF16, d_h in {64, 128}; rope_base finite and > 1
+ * (else INVALID_ARGUMENT); GQA_F32 returns UNSUPPORTED.  Otherwise as gqa_prefill.
+ */
+int gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
+                     int B, int h_q, int h_kv, int T, int d_h,
+                     int mask, const int32_t* kv_lens, float scale, float rope_base,
+                     int in_dtype, int out_dtype, void* stream);
+
+/*
+ * One decode step with rotary encoding: gqa_kv_append_rope (k_new rotated at
+ * write_pos[b]) followed by gqa_decode with each query rotated at its position
+ * p_b = q_pos[b] (q_pos == NULL: seq_lens[b] - 1), bit-identical to those two
+ * calls with gqa_rope applied to q at p_b.  As gqa_append_decode, the append
+ * runs inside the decode kernel when r <= 16.  Arguments as gqa_append_decode
+ * plus rope_base; supported and errors as gqa_prefill_rope.
+ */
+int gqa_append_decode_rope(const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int32_t* write_pos, const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                           int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+                           float scale, float rope_base, int in_dtype, int out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gqa_prefill that also writes the row log-sum-exp of the scaled scores,
  * lse[b][a][i] = log sum_j exp(scale q_i . k_j) over the visible keys (natural
  * log; -inf for a row with no visible key), fp32 (B, h_q, T).  These per-row

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
               "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged",
               "gqa_rope", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
-              "gqa_prefill_backward_workspace_bytes", "gqa_append_decode", "gqa_append_decode_paged"):
+              "gqa_prefill_backward_workspace_bytes", "gqa_append_decode", "gqa_append_decode_paged",
+              "gqa_prefill_rope", "gqa_append_decode_rope"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -251,3 +252,39 @@ def test_append_decode_validation():
     assert pcall(bt=None) == ops.GQA_ERR_INVALID_ARGUMENT
     assert pcall(page=48) == ops.GQA_ERR_UNSUPPORTED
     assert pcall(wsb=0) == ops.GQA_ERR_WORKSPACE_TOO_SMALL
+
+
+@needs_lib
+def test_rope_fused_validation():
+    """Prefill and decode with rotary encoding in the kernels: bad bases, the fp32
+    path and the usual argument errors are caught before any launch."""
+    lib = ops.load_library()
+    # (q, k, v, o, B, h_q, h_kv, T, d_h, mask, kv_lens, scale, base, in, out, stream)
+    ok = [FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, 128, ops.GQA_MASK_CAUSAL, None, 0.088, 10000.0, ops.GQA_BF16,
+          ops.GQA_F32, None]
+    def pre(**kw):
+        a = list(ok)
+        names = ["q", "k", "v", "o", "B", "h_q", "h_kv", "T", "d_h", "mask", "kv", "scale", "base", "in", "out", "s"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return lib.gqa_prefill_rope(*a)
+    assert pre(base=1.0) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert pre(base=float("nan")) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert pre(**{"in": ops.GQA_F32}) == ops.GQA_ERR_UNSUPPORTED
+    assert pre(d_h=96) == ops.GQA_ERR_UNSUPPORTED
+    assert pre(h_q=7) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert pre(q=FAKE + 8) == ops.GQA_ERR_INVALID_ARGUMENT
+    ws = lib.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128, ops.GQA_BF16)
+    dec = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 32, 8, 8192, 128, 0, 0.088, 10000.0,
+           ops.GQA_BF16, ops.GQA_F32, FAKE, ws, None]
+    def dcall(**kw):
+        a = list(dec)
+        names = ["q", "kc", "vc", "kn", "vn", "wp", "sl", "qp", "o", "B", "h_q", "h_kv", "T", "d_h", "msl", "scale",
+                 "base", "in", "out", "ws", "wsb", "s"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return lib.gqa_append_decode_rope(*a)
+    assert dcall(base=0.5) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert dcall(**{"in": ops.GQA_F32, "d_h": 40}) == ops.GQA_ERR_UNSUPPORTED
+    assert dcall(kn=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert dcall(wsb=ws - 1) == ops.GQA_ERR_WORKSPACE_TOO_SMALL

@@ -161,3 +161,58 @@ def test_rope_append_decode():
                                                              np.array([hist[b]])))).astype(np.float64)
         want = oracle.attention(qr, kr, v, causal=True, q_pos=np.array([[hist[b]]]), kv_len=np.array([L]))
         check_parity(got[b:b + 1], want, mode="bf16", what=f"rope decode b={b}")
+
+
+# ---------------------------------------------------------------- rotation inside the attention kernels
+@pytest.mark.parametrize("d,lens,out_dtype", [(128, None, None), (64, [700, 333], "bf16")],
+                         ids=["d128", "d64_padded_bf16out"])
+def test_prefill_rope_fused_equals_rope_then_prefill(d, lens, out_dtype):
+    """Q rotated as the prefill kernel loads it: bit-identical to gqa_rope on Q then
+    gqa_prefill, and within the bf16 bounds of the oracle over rotated rows."""
+    import torch
+
+    B, h_q, h_kv, T = 2, 8, 2, 700
+    print(f"case prefill_rope d={d} lens={lens}", flush=True)
+    x = inputs.make_prefill(B, h_q, h_kv, d, T, "bf16", 13500 + d)
+    qd, kd, vd = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    od = None if out_dtype is None else torch.bfloat16
+    kv = None if lens is None else ints_dev(lens)
+    krot = ops.gqa_rope(kd)
+    o_sep = ops.gqa_prefill(ops.gqa_rope(qd), krot, vd, kv_lens=kv, out_dtype=od)
+    o_fused = ops.gqa_prefill_rope(qd, krot, vd, kv_lens=kv, out_dtype=od)
+    torch.cuda.synchronize()
+    assert torch.equal(o_fused, o_sep)
+    if lens is None:
+        pos = np.arange(T)
+        qr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(x["q"], "bf16"), pos))).astype(np.float64)
+        kr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(x["k"], "bf16"), pos))).astype(np.float64)
+        want = oracle.attention(qr, kr, f64(x["v"], "bf16"), causal=True)
+        check_parity(to_host64(o_fused), want, mode="bf16", what="fused rope prefill")
+
+
+@pytest.mark.parametrize("h_q,h_kv,d,qpos", [(16, 4, 128, True), (8, 8, 64, False), (64, 2, 128, True)],
+                         ids=["r4", "mha_d64_default_pos", "r32_two_launches"])
+def test_append_decode_rope_equals_separate_calls(h_q, h_kv, d, qpos):
+    """The decode step with rotary encoding in one call -- new key rotated at its write
+    position, query at its position -- against gqa_kv_append_rope, gqa_rope on the
+    query and gqa_decode: same caches and output, bit for bit."""
+    import torch
+
+    B = 5
+    T_cap = inputs.round_up(2500 + 1, 64)
+    print(f"case append_decode_rope h_q={h_q} h_kv={h_kv} d={d}", flush=True)
+    x = inputs.make_append_decode(B, h_q, h_kv, d, T_cap, "bf16", 13600 + h_q + d, hist_hi=2500)
+    kd0 = ops.gqa_rope(to_dev(x["k_cache"], "bf16"))          # prompt keys, rotated at their positions
+    vd0 = to_dev(x["v_cache"], "bf16")
+    q, kn, vn = to_dev(x["q"], "bf16"), to_dev(x["k_new"], "bf16"), to_dev(x["v_new"], "bf16")
+    wp, sl, msl = ints_dev(x["write_pos"]), ints_dev(x["seq_lens"]), int(x["seq_lens"].max())
+    qp = ints_dev(x["q_pos"]) if qpos else None
+    k1, v1 = kd0.clone(), vd0.clone()
+    ops.gqa_kv_append_rope(k1, v1, kn, vn, wp)
+    o1 = ops.gqa_decode(ops.gqa_rope(q, pos0=ints_dev(x["q_pos"])), k1, v1, sl, q_pos=qp, max_seq_len=msl)
+    k2, v2 = kd0.clone(), vd0.clone()
+    o2 = ops.gqa_append_decode_rope(q, k2, v2, kn, vn, wp, sl, q_pos=qp, max_seq_len=msl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)) and torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+    assert bool(torch.isfinite(o2).all())
