@@ -79,7 +79,7 @@ __device__ __forceinline__ uint4 new_key_chunk(const DecodeParams& p, int b, int
     const uint4 y = *reinterpret_cast<const uint4*>(src + (lo ? c8 + HC : c8 - HC) * 8);
     bf16x8 a = __builtin_bit_cast(bf16x8, lo ? x : y), u = __builtin_bit_cast(bf16x8, lo ? y : x);
     const int i0 = (lo ? c8 : c8 - HC) * 8;
-    double th[8];
+    uint64_t th[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) th[e] = p.rope_theta.t[i0 + e];
     rope_rotate8(a, u, wp, th);
@@ -210,7 +210,7 @@ decode_bf16_kernel(DecodeParams p) {
       const int qp = query_position(p, b);
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        double th[8];
+        uint64_t th[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) th[e] = h ? p.rope_theta.t[16 * ks + 8 + e] : p.rope_theta.t[16 * ks + e];
         rope_rotate8(qf[ks], qf[ks + D / 32], qp, th);
@@ -517,10 +517,10 @@ decode16_bf16_kernel(DecodeParams p) {
       const int qp = query_position(p, b);
 #pragma unroll
       for (int kd = 0; kd < D / 64; ++kd) {
-        double th[8];
+        uint64_t th[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const double* t = p.rope_theta.t + 32 * kd + e;
+          const uint64_t* t = p.rope_theta.t + 32 * kd + e;
           th[e] = G == 0 ? t[0] : G == 1 ? t[8] : G == 2 ? t[16] : t[24];
         }
         rope_rotate8(qf[kd], qf[kd + D / 64], qp, th);

@@ -163,7 +163,7 @@ prefill_bf16_kernel(PrefillParams p) {
     for (int cc = 0; cc < PAIR_CH; cc += kThreads / 64) {
       const int c_ = cc + wave;                          // wave-uniform
       if (c_ < PAIR_CH) {
-        double th[8];
+        uint64_t th[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) th[e] = p.rope_theta.t[8 * c_ + e];
 #pragma unroll

@@ -9,7 +9,7 @@
 // never to rows already stored, which other readers may share ([Ch09] 09.4).
 //
 // The rotation (pair (x[i], x[i + d/2]) turned by p * base^(-2 i / d), angles
-// reduced to turns in double precision, hardware sine and cosine) is in
+// reduced to a fraction of a turn in fixed point, hardware sine and cosine) is in
 // rope_common.h, shared with the attention kernels that rotate Q as they load it.
 // Elements are read and written in the tensor's own precision; the arithmetic is fp32.
 #include "internal.h"
@@ -56,7 +56,7 @@ rope_kernel(const T* x, T* y, const int32_t* pos0, int H, int S, int half, long 
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
     float c, sn, y0, y1;
-    rope_cos_sin(p, f.inv_freq[i0 + v], c, sn);
+    rope_cos_sin(p, f.turn_frac[i0 + v], c, sn);
     rope_rotate(ld(l + v), ld(u + v), c, sn, y0, y1);
     st(l + v, y0);
     st(u + v, y1);
@@ -82,7 +82,7 @@ kv_append_rope_kernel(T* kc, T* vc, const T* kn, const T* vn, const int32_t* wri
   T* vd = vc + ((size_t)(b * h_kv + g) * T_cap + wp) * d;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
     float c, sn, y0, y1;
-    rope_cos_sin(wp, f.inv_freq[i], c, sn);
+    rope_cos_sin(wp, f.turn_frac[i], c, sn);
     rope_rotate(ld(ks + i), ld(ks + i + half), c, sn, y0, y1);
     st(kd + i, y0);
     st(kd + i + half, y1);

@@ -5,10 +5,11 @@
 // The pages print no rotation formula; the form used is the common one, pair
 // (x[i], x[i + d/2]) turned by the angle p * theta_i, theta_i = base^(-2 i / d):
 //     y[i]       = x[i] cos - x[i + d/2] sin,   y[i + d/2] = x[i + d/2] cos + x[i] sin.
-// theta_i comes from the host in double precision; the angle p * theta_i is formed
-// and reduced to a fraction of a turn in double precision (angles reach 3e4 radians
-// at the lengths served), and the hardware sine and cosine (which take turns) are
-// applied to that fraction in single precision.
+// theta_i / (2 pi) comes from the host as a 64-bit fixed-point fraction of a turn
+// F_i; the device forms p * F_i modulo 2^64 with integer products, which drops the
+// whole turns exactly (angles reach 3e4 radians at the lengths served) and leaves
+// the fraction, whose top 32 bits, read as a signed fraction in [-1/2, 1/2), feed
+// the hardware sine and cosine (which take turns) in single precision.
 #pragma once
 
 #include <cmath>
@@ -19,23 +20,26 @@
 namespace gqa {
 
 struct RopeFreq {
-  double inv_freq[kRopeMaxHalf];   // theta_i, i < d / 2
+  uint64_t turn_frac[kRopeMaxHalf];   // round(2^64 theta_i / (2 pi)), i < d / 2
 };
 
 inline RopeFreq make_rope_freq(int d, float base) {
   RopeFreq f;
   const int half = d / 2;
-  for (int i = 0; i < kRopeMaxHalf; ++i)
-    f.inv_freq[i] = i < half ? std::pow((double)base, -2.0 * i / d) : 0.0;
+  const long double two_pi = 6.283185307179586476925286766559L;
+  for (int i = 0; i < kRopeMaxHalf; ++i) {
+    if (i >= half) { f.turn_frac[i] = 0; continue; }
+    const long double turns = std::pow((long double)base, -2.0L * i / d) / two_pi;   // < 1 turn
+    f.turn_frac[i] = (uint64_t)std::llround(std::ldexp(turns, 63)) << 1;
+  }
   return f;
 }
 
-// cos and sin of p * theta: the angle is reduced in double precision to a fraction
-// of a turn in [-1/2, 1/2]; the hardware sine and cosine take that fraction.
-__device__ __forceinline__ void rope_cos_sin(int p, double theta, float& c, float& s) {
-  constexpr double kInv2Pi = 0.15915494309189533577;
-  const double turns = (double)p * theta * kInv2Pi;
-  const float f = (float)(turns - rint(turns));
+// cos and sin of p * theta for theta = 2 pi F / 2^64: p * F modulo 2^64 is the
+// fraction of a turn; its top 32 bits, signed, are that fraction in [-1/2, 1/2).
+__device__ __forceinline__ void rope_cos_sin(int p, uint64_t F, float& c, float& s) {
+  const uint64_t t = (uint64_t)(int64_t)p * F;
+  const float f = (float)(int32_t)(uint32_t)(t >> 32) * 0x1p-32f;
   c = __builtin_amdgcn_cosf(f);
   s = __builtin_amdgcn_sinf(f);
 }
@@ -53,24 +57,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// Angles theta_i of the head widths the attention kernels serve (d_h <= 128), as
+// Turn fractions F_i of the head widths the attention kernels serve (d_h <= 128), as
 // kernel arguments: a lane reads the entries its elements need with scalar loads
 // and a select, never by a lane-varying index into the argument block.
 constexpr int kRopeKernelHalf = 64;
 struct RopeTheta {
-  double t[kRopeKernelHalf];
+  uint64_t t[kRopeKernelHalf];       // the first entries of RopeFreq::turn_frac
 };
 
 inline RopeTheta make_rope_theta(int d, float base) {
   const RopeFreq f = make_rope_freq(d, base);
   RopeTheta r;
-  for (int i = 0; i < kRopeKernelHalf; ++i) r.t[i] = f.inv_freq[i];
+  for (int i = 0; i < kRopeKernelHalf; ++i) r.t[i] = f.turn_frac[i];
   return r;
 }
 
 // Rotate the bf16 pairs (lo[e], hi[e]), e < 8, of one row at position p: lo[e] is
-// element i_e of the first half, hi[e] its partner i_e + d/2, th[e] = theta_{i_e}.
-__device__ __forceinline__ void rope_rotate8(bf16x8& lo, bf16x8& hi, int p, const double (&th)[8]) {
+// element i_e of the first half, hi[e] its partner i_e + d/2, th[e] = F_{i_e}.
+__device__ __forceinline__ void rope_rotate8(bf16x8& lo, bf16x8& hi, int p, const uint64_t (&th)[8]) {
   typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
   u16x8 l = __builtin_bit_cast(u16x8, lo), u = __builtin_bit_cast(u16x8, hi);
 #pragma unroll
