@@ -114,6 +114,12 @@ def time_calls(fn, steps: int, warmup: int, flush=None):
     return wall, [a.elapsed_time(b) for a, b in evs]
 
 
+def spread(per):
+    """Median and minimum of per-call milliseconds (the mean is the reported value)."""
+    t = sorted(per)
+    return {"ms_median": round(t[len(t) // 2], 5), "ms_min": round(t[0], 5)}
+
+
 def time_region(fn, steps: int, warmup: int):
     """Run fn warmup+steps times back to back; one HIP event pair on the current stream
     around the timed launches.  Returns (wall seconds of the timed region, average ms per
@@ -255,7 +261,7 @@ def bench_decode(name, steps, warmup, flush_buf, page_size=0):
     wname = w.name + (f"_paged{page_size}" if page_size else "")
     res = {
         "workload": wname, "B": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "d_h": w.d_h, "T_cap": w.T,
-        "max_seq_len": msl, "algorithmic_bytes": nbytes, "ms_per_call": round(kern_ms, 5),
+        "max_seq_len": msl, "algorithmic_bytes": nbytes, "ms_per_call": round(kern_ms, 5), **spread(per),
         "value": round(gbs, 1), "unit": "GB/s",
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -335,7 +341,8 @@ def bench_rope(steps, warmup, flush_buf):
     _, sep_ms = time_region(lambda: (ops.gqa_rope(q, out=qo), ops.gqa_prefill(qo, ko, v, out=out)), steps, warmup)
     del v, out
     return {"workload": w.name + "_qk_rope", "rows": w.B * (w.h_q + w.h_kv) * w.T, "d_h": w.d_h,
-            "algorithmic_bytes": nbytes, "ms_per_call": round(ms, 5), "value": round(gbs, 1), "unit": "GB/s",
+            "algorithmic_bytes": nbytes, "ms_per_call": round(ms, 5), **spread(per), "value": round(gbs, 1),
+            "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
             "kernels": "rope (Q) + rope (K)",
