@@ -62,10 +62,10 @@ int run_attention(const AttnArgs& a, int in_dtype, void* stream) {
 
 extern "C" {
 
-int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,
-                      int B, int h_q, int h_kv, int S_q, int T_cap, int d_h,
-                      int mask, const int32_t* kv_lens, const int32_t* q_pos0,
-                      float scale, int in_dtype, int out_dtype, void* stream) {
+static int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, void* o,
+                              int B, int h_q, int h_kv, int S_q, int T_cap, int d_h,
+                              int mask, const int32_t* kv_lens, const int32_t* q_pos0,
+                              float scale, int in_dtype, int out_dtype, void* stream, float rope_base) {
   if (B < 1 || h_q < 1 || h_kv < 1 || S_q < 1 || T_cap < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (mask != GQA_MASK_NONE && mask != GQA_MASK_CAUSAL) return GQA_ERR_INVALID_ARGUMENT;
@@ -85,7 +85,26 @@ int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
   a.q_pos_from_end = 1;
   a.scale = scale;
   a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
+  a.rope_base = rope_base;
   return run_attention(a, in_dtype, stream);
+}
+
+int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,
+                      int B, int h_q, int h_kv, int S_q, int T_cap, int d_h,
+                      int mask, const int32_t* kv_lens, const int32_t* q_pos0,
+                      float scale, int in_dtype, int out_dtype, void* stream) {
+  return prefill_chunk_impl(q, k_cache, v_cache, o, B, h_q, h_kv, S_q, T_cap, d_h, mask, kv_lens, q_pos0, scale,
+                            in_dtype, out_dtype, stream, 0.f);
+}
+
+int gqa_prefill_chunk_rope(const void* q, const void* k_cache, const void* v_cache, void* o,
+                           int B, int h_q, int h_kv, int S_q, int T_cap, int d_h,
+                           int mask, const int32_t* kv_lens, const int32_t* q_pos0,
+                           float scale, float rope_base, int in_dtype, int out_dtype, void* stream) {
+  if (!std::isfinite(rope_base) || rope_base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  if (known_dtype(in_dtype) && in_dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  return prefill_chunk_impl(q, k_cache, v_cache, o, B, h_q, h_kv, S_q, T_cap, d_h, mask, kv_lens, q_pos0, scale,
+                            in_dtype, out_dtype, stream, rope_base);
 }
 
 static int prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -40,6 +40,7 @@ SIGNATURES = {
     "gqa_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gqa_append_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "gqa_prefill_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _F, _I, _I, _P]),
+    "gqa_prefill_chunk_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _F, _F, _I, _I, _P]),
     "gqa_append_decode_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I,
                                     _P, _S, _P]),
     "gqa_append_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -207,6 +208,16 @@ def gqa_prefill_rope(q, k, v, *, causal: bool = True, scale: Optional[float] = N
 def gqa_prefill_chunk(q, k_cache, v_cache, *, kv_lens=None, q_pos0=None, causal: bool = True,
                       scale: Optional[float] = None, out=None, out_dtype=None):
     """S_q queries per sequence at absolute positions q_pos0[b] + i against a cache."""
+    return _prefill_chunk(q, k_cache, v_cache, kv_lens, q_pos0, causal, scale, out, out_dtype, None)
+
+
+def gqa_prefill_chunk_rope(q, k_cache, v_cache, *, kv_lens=None, q_pos0=None, causal: bool = True,
+                           scale: Optional[float] = None, base: float = 10000.0, out=None, out_dtype=None):
+    """gqa_prefill_chunk with each query row rotated at its absolute position inside the kernel."""
+    return _prefill_chunk(q, k_cache, v_cache, kv_lens, q_pos0, causal, scale, out, out_dtype, float(base))
+
+
+def _prefill_chunk(q, k_cache, v_cache, kv_lens, q_pos0, causal, scale, out, out_dtype, rope_base):
     torch = _torch()
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev_tensor(t, n, 4)
@@ -225,9 +236,13 @@ def gqa_prefill_chunk(q, k_cache, v_cache, *, kv_lens=None, q_pos0=None, causal:
     q_pos0 = _int_vec(q_pos0, "q_pos0", B, q.device)
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
     lib = load_library()
-    _launch(q.device, (("k_cache", k_cache), ("v_cache", v_cache), ("out", out)), lib.gqa_prefill_chunk,
-            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, h_q, h_kv, S_q, T_cap, d_h,
-            GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), _ptr(q_pos0), sc, code, oc)
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, h_q, h_kv, S_q, T_cap, d_h,
+            GQA_MASK_CAUSAL if causal else GQA_MASK_NONE, _ptr(kv_lens), _ptr(q_pos0), sc)
+    tensors = (("k_cache", k_cache), ("v_cache", v_cache), ("out", out))
+    if rope_base is None:
+        _launch(q.device, tensors, lib.gqa_prefill_chunk, *head, code, oc)
+    else:
+        _launch(q.device, tensors, lib.gqa_prefill_chunk_rope, *head, rope_base, code, oc)
     return out
 
 

@@ -241,6 +241,16 @@ int gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
                      int in_dtype, int out_dtype, void* stream);
 
 /*
+ * gqa_prefill_chunk with query row i of sequence b rotated at its absolute
+ * position q_pos0[b] + i (q_pos0 == NULL: kv_lens[b] - S_q + i, as there).
+ * Supported and errors as gqa_prefill_rope; otherwise as gqa_prefill_chunk.
+ */
+int gqa_prefill_chunk_rope(const void* q, const void* k_cache, const void* v_cache, void* o,
+                           int B, int h_q, int h_kv, int S_q, int T_cap, int d_h,
+                           int mask, const int32_t* kv_lens, const int32_t* q_pos0,
+                           float scale, float rope_base, int in_dtype, int out_dtype, void* stream);
+
+/*
  * One decode step with rotary encoding: gqa_kv_append_rope (k_new rotated at
  * write_pos[b]) followed by gqa_decode with each query rotated at its position
  * p_b = q_pos[b] (q_pos == NULL: seq_lens[b] - 1), bit-identical to those two

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
               "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged",
               "gqa_rope", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
               "gqa_prefill_backward_workspace_bytes", "gqa_append_decode", "gqa_append_decode_paged",
-              "gqa_prefill_rope", "gqa_append_decode_rope"):
+              "gqa_prefill_rope", "gqa_append_decode_rope", "gqa_prefill_chunk_rope"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -274,6 +274,12 @@ def test_rope_fused_validation():
     assert pre(d_h=96) == ops.GQA_ERR_UNSUPPORTED
     assert pre(h_q=7) == ops.GQA_ERR_INVALID_ARGUMENT
     assert pre(q=FAKE + 8) == ops.GQA_ERR_INVALID_ARGUMENT
+    # chunked: (q, kc, vc, o, B, h_q, h_kv, S_q, T_cap, d_h, mask, kv_lens, q_pos0, scale, base, in, out, stream)
+    ch = [FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 16, 64, 128, ops.GQA_MASK_CAUSAL, None, None, 0.088, 10000.0,
+          ops.GQA_BF16, ops.GQA_F32, None]
+    assert lib.gqa_prefill_chunk_rope(*(ch[:14] + [0.0] + ch[15:])) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert lib.gqa_prefill_chunk_rope(*(ch[:15] + [ops.GQA_F32] + ch[16:])) == ops.GQA_ERR_UNSUPPORTED
+    assert lib.gqa_prefill_chunk_rope(*(ch[:12] + [FAKE + 2] + ch[13:])) == ops.GQA_ERR_INVALID_ARGUMENT
     ws = lib.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128, ops.GQA_BF16)
     dec = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 32, 8, 8192, 128, 0, 0.088, 10000.0,
            ops.GQA_BF16, ops.GQA_F32, FAKE, ws, None]

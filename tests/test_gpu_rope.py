@@ -216,3 +216,25 @@ def test_append_decode_rope_equals_separate_calls(h_q, h_kv, d, qpos):
     assert torch.equal(o1, o2)
     assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)) and torch.equal(v1.view(torch.int16), v2.view(torch.int16))
     assert bool(torch.isfinite(o2).all())
+
+
+@pytest.mark.parametrize("explicit_pos", [True, False], ids=["q_pos0", "newest_rows"])
+def test_prefill_chunk_rope_equals_rope_then_chunk(explicit_pos):
+    """Chunked prefill with Q rotated in the kernel at each row's absolute position:
+    bit-identical to gqa_rope at those positions followed by gqa_prefill_chunk."""
+    import torch
+
+    B, h_q, h_kv, S_q, T_cap, d = 3, 16, 4, 100, 1000, 128
+    print(f"case prefill_chunk_rope explicit={explicit_pos}", flush=True)
+    x = inputs.make_decode(B, h_q, h_kv, d, T_cap, "bf16", 13700, seq_lens=[1000, 640, 101])
+    q = to_dev(inputs.normal(13700, "q", (B, h_q, S_q, d), "bf16"), "bf16")
+    kc = ops.gqa_rope(to_dev(x["k_cache"], "bf16"))
+    vc = to_dev(x["v_cache"], "bf16")
+    lens = np.array([1000, 640, 101], np.int32)
+    pos0 = np.array([900, 200, 1], np.int32) if explicit_pos else lens - S_q
+    qp = ints_dev(pos0) if explicit_pos else None
+    o_sep = ops.gqa_prefill_chunk(ops.gqa_rope(q, pos0=ints_dev(pos0)), kc, vc, kv_lens=ints_dev(lens), q_pos0=qp)
+    o_fused = ops.gqa_prefill_chunk_rope(q, kc, vc, kv_lens=ints_dev(lens), q_pos0=qp)
+    torch.cuda.synchronize()
+    assert torch.equal(o_fused, o_sep)
+    assert bool(torch.isfinite(o_fused).all())
