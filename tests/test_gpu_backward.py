@@ -150,3 +150,28 @@ def test_backward_prefill_workload_sampled():
         _check_grad(dk[0, g, lo:], dkw[0, 0, lo:], f"full-size dK tail g={g}")
         _check_grad(dv[0, g, lo:], dvw[0, 0, lo:], f"full-size dV tail g={g}")
     assert np.max(np.abs(dk.sum(axis=2))) <= 1e-3 * np.max(np.abs(dk)) * np.sqrt(w.T)
+
+
+@pytest.mark.parametrize("o_dtype", ["f32", "bf16"])
+def test_backward_with_o_not_16_byte_aligned(o_dtype):
+    """delta = rowsum(dO * O) reads O with 16-byte loads when O is 16-byte aligned and
+    element by element otherwise; an O that starts one element into a buffer takes the
+    second path and gives gradients within the same bar of the oracle."""
+    import torch
+
+    B, h_q, h_kv, T, d = 1, 8, 2, 150, 128
+    print(f"case backward misaligned O {o_dtype}", flush=True)
+    x = inputs.make_prefill(B, h_q, h_kv, d, T, "bf16", 14800)
+    d_out = inputs.normal(14800, "d_out", (B, h_q, T, d), "bf16")
+    q, k, v, do = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(d_out, "bf16")
+    od = torch.float32 if o_dtype == "f32" else torch.bfloat16
+    o, lse = ops.gqa_prefill_lse(q, k, v, out_dtype=od)
+    buf = torch.empty(o.numel() + 1, dtype=od, device=o.device)
+    o_off = buf[1:].view(o.shape)
+    o_off.copy_(o)
+    assert o_off.data_ptr() % 16 != 0
+    grads = ops.gqa_prefill_backward(q, k, v, o_off, do, lse)
+    torch.cuda.synchronize()
+    want = _oracle(x, d_out, True)
+    for name, g, w in zip(("dq", "dk", "dv"), grads, want):
+        _check_grad(to_host64(g), w, f"misaligned O {o_dtype} {name}")
