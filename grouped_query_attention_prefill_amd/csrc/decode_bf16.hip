@@ -19,6 +19,11 @@
 // 16x16 matrix-core tiles (16 keys per wave per 64-key tile), which halves the
 // accumulator registers so that more workgroups share a CU and keep more HBM
 // requests in flight; larger groups use 32x32 tiles over 128-key tiles.
+// Grid rows take the sequences longest first.  The 16x16 kernel can also do the
+// decode step's append ([AttnVar] 3.1: the new token's K/V are written, then all
+// visible rows are read): the workgroup whose tiles hold the new row writes it
+// and reads the new values in its place.  The ROPE instances rotate Q (and the
+// appended key) as they load them.
 #include "internal.h"
 #include "mfma_common.h"
 #include "rope_common.h"

@@ -31,7 +31,8 @@
 // a double-buffered LDS stage, written in the middle of the group's matrix phase
 // (global loads are requested two phases before their data is written).  A
 // matrix phase opens with a few QK products whose K operands were read before
-// its barrier.
+// its barrier.  The ROPE instances rotate the workgroup's Q rows at their
+// positions (in LDS, once the first tile's loads are issued) before the loop.
 //
 // Layouts in LDS, both filled by 16-byte buffer loads that return zeros past the
 // last visible key (no per-load branches):
