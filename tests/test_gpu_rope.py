@@ -238,3 +238,29 @@ def test_prefill_chunk_rope_equals_rope_then_chunk(explicit_pos):
     torch.cuda.synchronize()
     assert torch.equal(o_fused, o_sep)
     assert bool(torch.isfinite(o_fused).all())
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_append_decode_rope_edge_positions(d):
+    """Write positions on tile edges, past the visible keys (written rotated, never
+    read) and outside the cache (skipped): the fused rotating step leaves the same
+    caches and output as gqa_kv_append_rope, gqa_rope on the query and gqa_decode."""
+    import torch
+
+    B, h_q, h_kv, T_cap = 6, 16, 2, 1024
+    lens = np.array([1000, 64, 65, 500, 300, 9], np.int32)
+    wp = np.array([999, 63, 64, 505, -1, 1024], np.int32)
+    print(f"case append_decode_rope edges d={d}", flush=True)
+    x = inputs.make_decode(B, h_q, h_kv, d, T_cap, "bf16", 13800 + d, seq_lens=lens, poison=True)
+    kn = to_dev(inputs.normal(13800 + d, "k_new", (B, h_kv, 1, d), "bf16"), "bf16")
+    vn = to_dev(inputs.normal(13800 + d, "v_new", (B, h_kv, 1, d), "bf16"), "bf16")
+    k0, v0 = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+    q, sl, wpd = to_dev(x["q"], "bf16"), ints_dev(lens), ints_dev(wp)
+    k1, v1 = k0.clone(), v0.clone()
+    ops.gqa_kv_append_rope(k1, v1, kn, vn, wpd)
+    o1 = ops.gqa_decode(ops.gqa_rope(q, pos0=ints_dev(lens - 1)), k1, v1, sl)
+    k2, v2 = k0.clone(), v0.clone()
+    o2 = ops.gqa_append_decode_rope(q, k2, v2, kn, vn, wpd, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)) and torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+    assert torch.equal(o1, o2)
