@@ -277,7 +277,8 @@ static int decode_paged_impl(const void* q, const void* k_pages, const void* v_p
                              const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos, void* o,
                              int B, int h_q, int h_kv, int page_size, int n_pages, int max_pages_per_seq, int d_h,
                              int max_seq_len, float scale, int in_dtype, int out_dtype,
-                             void* workspace, size_t workspace_bytes, void* stream, const AppendIn* ap) {
+                             void* workspace, size_t workspace_bytes, void* stream, const AppendIn* ap,
+                             float rope_base = 0.f) {
   if (B < 1 || h_q < 1 || h_kv < 1 || page_size < 1 || n_pages < 1 || max_pages_per_seq < 1 || d_h < 1)
     return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
@@ -297,6 +298,7 @@ static int decode_paged_impl(const void* q, const void* k_pages, const void* v_p
   if (ap && !append_ptrs_ok(*ap, k_pages, v_pages, d_h, 2)) return GQA_ERR_INVALID_ARGUMENT;
   const int len = max_seq_len > 0 ? max_seq_len : T_cap;
   DecodeArgs a;
+  a.rope_base = rope_base;
   a.q = q; a.k = k_pages; a.v = v_pages; a.seq_lens = seq_lens; a.q_pos = q_pos; a.o = o;
   a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.T_cap = T_cap; a.D = d_h; a.max_len = len;
   a.scale = scale;
@@ -311,9 +313,14 @@ static int decode_paged_impl(const void* q, const void* k_pages, const void* v_p
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fused = ap && h_q / h_kv <= 16;
   if (ap && !fused) {
-    const hipError_t e = gqa::launch_kv_append_paged(const_cast<void*>(k_pages), const_cast<void*>(v_pages),
-                                                     ap->k_new, ap->v_new, block_table, ap->write_pos, B, h_kv,
-                                                     page_size, n_pages, max_pages_per_seq, d_h, 2, s);
+    const hipError_t e =
+        rope_base != 0.f
+            ? gqa::launch_kv_append_paged_rope(const_cast<void*>(k_pages), const_cast<void*>(v_pages), ap->k_new,
+                                               ap->v_new, block_table, ap->write_pos, B, h_kv, page_size, n_pages,
+                                               max_pages_per_seq, d_h, rope_base, 2, s)
+            : gqa::launch_kv_append_paged(const_cast<void*>(k_pages), const_cast<void*>(v_pages), ap->k_new,
+                                          ap->v_new, block_table, ap->write_pos, B, h_kv, page_size, n_pages,
+                                          max_pages_per_seq, d_h, 2, s);
     if (e != hipSuccess) return GQA_ERR_HIP;
   }
   if (fused) { a.k_new = ap->k_new; a.v_new = ap->v_new; a.write_pos = ap->write_pos; }
@@ -369,6 +376,38 @@ int gqa_append_decode_paged(const void* q, void* k_pages, void* v_pages, const v
   return decode_paged_impl(q, k_pages, v_pages, block_table, seq_lens, q_pos, o, B, h_q, h_kv, page_size, n_pages,
                            max_pages_per_seq, d_h, max_seq_len, scale, in_dtype, out_dtype, workspace,
                            workspace_bytes, stream, &ap);
+}
+
+int gqa_append_decode_paged_rope(const void* q, void* k_pages, void* v_pages, const void* k_new,
+                                 const void* v_new, const int32_t* block_table, const int32_t* write_pos,
+                                 const int32_t* seq_lens, const int32_t* q_pos, void* o, int B, int h_q, int h_kv,
+                                 int page_size, int n_pages, int max_pages_per_seq, int d_h, int max_seq_len,
+                                 float scale, float rope_base, int in_dtype, int out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!std::isfinite(rope_base) || rope_base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  const AppendIn ap{k_new, v_new, write_pos};
+  return decode_paged_impl(q, k_pages, v_pages, block_table, seq_lens, q_pos, o, B, h_q, h_kv, page_size, n_pages,
+                           max_pages_per_seq, d_h, max_seq_len, scale, in_dtype, out_dtype, workspace,
+                           workspace_bytes, stream, &ap, rope_base);
+}
+
+int gqa_kv_append_paged_rope(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                             const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
+                             int page_size, int n_pages, int max_pages_per_seq, int d_h, float base, int dtype,
+                             void* stream) {
+  if (B < 1 || h_kv < 1 || page_size < 1 || n_pages < 1 || max_pages_per_seq < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if ((long long)page_size * max_pages_per_seq > 0x7fffffffLL) return GQA_ERR_INVALID_ARGUMENT;
+  if (d_h < 2 || d_h % 2 != 0 || d_h / 2 > gqa::kRopeMaxHalf) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(base) || base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+  const int eb = dtype == GQA_BF16 ? 2 : 4;
+  if (!k_pages || !v_pages || !k_new || !v_new || !block_table || !write_pos) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_pages, eb) || !aligned(v_pages, eb) || !aligned(k_new, eb) || !aligned(v_new, eb) ||
+      !aligned(block_table, 4) || !aligned(write_pos, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  return hip_status(gqa::launch_kv_append_paged_rope(k_pages, v_pages, k_new, v_new, block_table, write_pos, B, h_kv,
+                                                     page_size, n_pages, max_pages_per_seq, d_h, base, eb,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 int gqa_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,

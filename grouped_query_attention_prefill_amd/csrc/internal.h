@@ -116,6 +116,10 @@ hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H
 hipError_t launch_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                                  const int32_t* write_pos, int B, int h_kv, int T_cap, int D, float base,
                                  int elem_bytes, hipStream_t s);
+hipError_t launch_kv_append_paged_rope(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                                       const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
+                                       int page_size, int n_pages, int max_pages, int D, float base, int elem_bytes,
+                                       hipStream_t s);
 hipError_t launch_kv_append_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
                                   const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
                                   int page_size, int n_pages, int max_pages, int D, int elem_bytes,

@@ -66,20 +66,29 @@ rope_kernel(const T* x, T* y, const int32_t* pos0, int H, int S, int half, long 
 }
 
 // Append with the key rotated at its own position: one workgroup per (K/V head,
-// sequence); threads < d/2 rotate key pairs, all threads copy the value row.
+// sequence); threads < d/2 rotate key pairs, all threads copy the value row.  With
+// a block table (paged pools (n_pages, h_kv, page_size, d)) the row is found through
+// the sequence's page, and a page outside the pool skips the sequence.
 template <typename T>
 __global__ void __launch_bounds__(128)
 kv_append_rope_kernel(T* kc, T* vc, const T* kn, const T* vn, const int32_t* write_pos, int h_kv,
-                      int T_cap, int half, RopeFreq f) {
+                      int T_cap, int half, RopeFreq f, const int32_t* block_table, int page_size,
+                      int n_pages, int max_pages) {
   const int g = blockIdx.x;
   const int b = blockIdx.y;
   const int wp = write_pos[b];
   if (wp < 0 || wp >= T_cap) return;
   const int d = 2 * half;
+  size_t row = ((size_t)(b * h_kv + g) * T_cap + wp) * d;
+  if (block_table) {
+    const int pg = block_table[(size_t)b * max_pages + wp / page_size];
+    if (pg < 0 || pg >= n_pages) return;
+    row = (((size_t)pg * h_kv + g) * page_size + wp % page_size) * d;
+  }
   const T* ks = kn + (size_t)(b * h_kv + g) * d;
   const T* vs = vn + (size_t)(b * h_kv + g) * d;
-  T* kd = kc + ((size_t)(b * h_kv + g) * T_cap + wp) * d;
-  T* vd = vc + ((size_t)(b * h_kv + g) * T_cap + wp) * d;
+  T* kd = kc + row;
+  T* vd = vc + row;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
     float c, sn, y0, y1;
     rope_cos_sin(wp, f.turn_frac[i], c, sn);
@@ -117,20 +126,38 @@ hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H
   return hipGetLastError();
 }
 
-hipError_t launch_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
-                                 const int32_t* write_pos, int B, int h_kv, int T_cap, int D, float base,
-                                 int elem_bytes, hipStream_t s) {
+namespace {
+hipError_t append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* write_pos, int B, int h_kv, int T_cap, int D, float base, int elem_bytes,
+                       const int32_t* block_table, int page_size, int n_pages, int max_pages, hipStream_t s) {
   const RopeFreq f = make_rope_freq(D, base);
   if (elem_bytes == 4)
     hipLaunchKernelGGL(kv_append_rope_kernel<float>, dim3(h_kv, B), dim3(128), 0, s,
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), static_cast<const float*>(k_new),
-                       static_cast<const float*>(v_new), write_pos, h_kv, T_cap, D / 2, f);
+                       static_cast<const float*>(v_new), write_pos, h_kv, T_cap, D / 2, f, block_table, page_size,
+                       n_pages, max_pages);
   else
     hipLaunchKernelGGL(kv_append_rope_kernel<uint16_t>, dim3(h_kv, B), dim3(128), 0, s,
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), write_pos, h_kv,
-                       T_cap, D / 2, f);
+                       T_cap, D / 2, f, block_table, page_size, n_pages, max_pages);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                 const int32_t* write_pos, int B, int h_kv, int T_cap, int D, float base,
+                                 int elem_bytes, hipStream_t s) {
+  return append_rope(k_cache, v_cache, k_new, v_new, write_pos, B, h_kv, T_cap, D, base, elem_bytes, nullptr, 0, 0,
+                     0, s);
+}
+
+hipError_t launch_kv_append_paged_rope(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                                       const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
+                                       int page_size, int n_pages, int max_pages, int D, float base, int elem_bytes,
+                                       hipStream_t s) {
+  return append_rope(k_pages, v_pages, k_new, v_new, write_pos, B, h_kv, page_size * max_pages, D, base, elem_bytes,
+                     block_table, page_size, n_pages, max_pages, s);
 }
 
 }  // namespace gqa

@@ -41,6 +41,9 @@ SIGNATURES = {
     "gqa_append_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "gqa_prefill_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _F, _I, _I, _P]),
     "gqa_prefill_chunk_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _F, _F, _I, _I, _P]),
+    "gqa_kv_append_paged_rope": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "gqa_append_decode_paged_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                          _F, _F, _I, _I, _P, _S, _P]),
     "gqa_append_decode_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I,
                                     _P, _S, _P]),
     "gqa_append_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -374,6 +377,20 @@ def gqa_append_decode_paged(q, k_pages, v_pages, k_new, v_new, block_table, writ
                             scale: Optional[float] = None, max_seq_len: Optional[int] = None, out=None,
                             out_dtype=None, workspace=None):
     """gqa_kv_append_paged then gqa_decode_paged on the same page pools, in one call."""
+    return _append_decode_paged(q, k_pages, v_pages, k_new, v_new, block_table, write_pos, seq_lens, q_pos, scale,
+                                max_seq_len, out, out_dtype, workspace, None)
+
+
+def gqa_append_decode_paged_rope(q, k_pages, v_pages, k_new, v_new, block_table, write_pos, seq_lens, *,
+                                 q_pos=None, scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                                 base: float = 10000.0, out=None, out_dtype=None, workspace=None):
+    """gqa_kv_append_paged_rope then gqa_decode_paged with each query rotated at its position, in one call."""
+    return _append_decode_paged(q, k_pages, v_pages, k_new, v_new, block_table, write_pos, seq_lens, q_pos, scale,
+                                max_seq_len, out, out_dtype, workspace, float(base))
+
+
+def _append_decode_paged(q, k_pages, v_pages, k_new, v_new, block_table, write_pos, seq_lens, q_pos, scale,
+                         max_seq_len, out, out_dtype, workspace, rope_base):
     torch = _torch()
     for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
         _dev_tensor(t, n, 4)
@@ -404,11 +421,15 @@ def gqa_append_decode_paged(q, k_pages, v_pages, k_new, v_new, block_table, writ
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
     msl = 0 if max_seq_len is None else int(max_seq_len)
-    _launch(q.device, (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table), ("out", out),
-                       ("workspace", workspace)),
-            lib.gqa_append_decode_paged, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new),
-            _ptr(block_table), _ptr(write_pos), _ptr(seq_lens), _ptr(q_pos), _ptr(out), B, h_q, h_kv, page_size,
-            n_pages, max_pages, d_h, msl, sc, code, oc, _ptr(workspace), ws_have)
+    head = (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(write_pos),
+            _ptr(seq_lens), _ptr(q_pos), _ptr(out), B, h_q, h_kv, page_size, n_pages, max_pages, d_h, msl, sc)
+    tail = (code, oc, _ptr(workspace), ws_have)
+    tensors = (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table), ("out", out),
+               ("workspace", workspace))
+    if rope_base is None:
+        _launch(q.device, tensors, lib.gqa_append_decode_paged, *head, *tail)
+    else:
+        _launch(q.device, tensors, lib.gqa_append_decode_paged_rope, *head, rope_base, *tail)
     return out
 
 
@@ -490,6 +511,27 @@ def gqa_rope(x, *, pos0=None, base: float = ROPE_BASE, out=None):
     _launch(x.device, (("out", out),), load_library().gqa_rope,
             _ptr(x), _ptr(out), _ptr(pos0), B, H, S, d_h, float(base), _dtype_code(x))
     return out
+
+
+def gqa_kv_append_paged_rope(k_pages, v_pages, k_new, v_new, block_table, write_pos, *, base: float = ROPE_BASE):
+    """gqa_kv_append_paged with k_new rotated at position write_pos[b] (in place on the pools)."""
+    torch = _torch()
+    for n, t in (("k_pages", k_pages), ("v_pages", v_pages), ("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, n, 4)
+    n_pages, h_kv, page_size, d_h = k_pages.shape
+    B = k_new.shape[0]
+    _require(v_pages.shape == k_pages.shape, "page pools must match")
+    _require(tuple(k_new.shape) == (B, h_kv, 1, d_h) and k_new.shape == v_new.shape, "k_new, v_new must be (B, h_kv, 1, d_h)")
+    _require(k_pages.dtype == v_pages.dtype == k_new.dtype == v_new.dtype, "dtypes must match")
+    _dev_tensor(block_table, "block_table", 2)
+    _require(block_table.dtype == torch.int32 and block_table.shape[0] == B, "block_table must be int32 (B, max_pages)")
+    write_pos = _int_vec(write_pos, "write_pos", B, k_pages.device)
+    _require(write_pos is not None, "write_pos is required")
+    _launch(k_pages.device, (("v_pages", v_pages), ("k_new", k_new), ("v_new", v_new), ("block_table", block_table)),
+            load_library().gqa_kv_append_paged_rope, _ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new),
+            _ptr(block_table), _ptr(write_pos), B, h_kv, page_size, n_pages, block_table.shape[1], d_h, float(base),
+            _dtype_code(k_pages))
+    return k_pages, v_pages
 
 
 def gqa_kv_append_rope(k_cache, v_cache, k_new, v_new, write_pos, *, base: float = ROPE_BASE):

@@ -265,6 +265,25 @@ int gqa_append_decode_rope(const void* q, void* k_cache, void* v_cache, const vo
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged forms of the rotating calls: gqa_kv_append_paged_rope is
+ * gqa_kv_append_paged with the new key rotated at write_pos[b] (supported and
+ * errors as gqa_kv_append_rope, plus the paged arguments' errors), and
+ * gqa_append_decode_paged_rope is gqa_kv_append_paged_rope followed by
+ * gqa_decode_paged with each query rotated at its position, bit-identical to
+ * those calls with gqa_rope applied to q, fused as gqa_append_decode_paged is.
+ */
+int gqa_kv_append_paged_rope(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                             const int32_t* block_table, const int32_t* write_pos, int B, int h_kv,
+                             int page_size, int n_pages, int max_pages_per_seq, int d_h, float base, int dtype,
+                             void* stream);
+int gqa_append_decode_paged_rope(const void* q, void* k_pages, void* v_pages, const void* k_new,
+                                 const void* v_new, const int32_t* block_table, const int32_t* write_pos,
+                                 const int32_t* seq_lens, const int32_t* q_pos, void* o, int B, int h_q, int h_kv,
+                                 int page_size, int n_pages, int max_pages_per_seq, int d_h, int max_seq_len,
+                                 float scale, float rope_base, int in_dtype, int out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * gqa_prefill that also writes the row log-sum-exp of the scaled scores,
  * lse[b][a][i] = log sum_j exp(scale q_i . k_j) over the visible keys (natural
  * log; -inf for a row with no visible key), fp32 (B, h_q, T).  These per-row

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
               "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged",
               "gqa_rope", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
               "gqa_prefill_backward_workspace_bytes", "gqa_append_decode", "gqa_append_decode_paged",
-              "gqa_prefill_rope", "gqa_append_decode_rope", "gqa_prefill_chunk_rope"):
+              "gqa_prefill_rope", "gqa_append_decode_rope", "gqa_prefill_chunk_rope", "gqa_kv_append_paged_rope",
+              "gqa_append_decode_paged_rope"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -294,3 +295,28 @@ def test_rope_fused_validation():
     assert dcall(**{"in": ops.GQA_F32, "d_h": 40}) == ops.GQA_ERR_UNSUPPORTED
     assert dcall(kn=None) == ops.GQA_ERR_INVALID_ARGUMENT
     assert dcall(wsb=ws - 1) == ops.GQA_ERR_WORKSPACE_TOO_SMALL
+
+
+@needs_lib
+def test_paged_rope_validation():
+    lib = ops.load_library()
+    # (kp, vp, kn, vn, bt, wp, B, h_kv, page, n_pages, max_pages, d_h, base, dtype, stream)
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 10, 4, 128, 10000.0, ops.GQA_BF16, None]
+    def app(i, v):
+        a = list(ok); a[i] = v
+        return lib.gqa_kv_append_paged_rope(*a)
+    assert app(4, None) == ops.GQA_ERR_INVALID_ARGUMENT        # no block table
+    assert app(12, 1.0) == ops.GQA_ERR_INVALID_ARGUMENT        # base
+    assert app(11, 3) == ops.GQA_ERR_UNSUPPORTED               # odd d_h
+    assert app(6, 0) == ops.GQA_ERR_INVALID_ARGUMENT           # B
+    # (q, kp, vp, kn, vn, bt, wp, sl, qp, o, B, h_q, h_kv, page, n_pages, max_pages, d_h, msl, scale, base, in, out,
+    #  ws, wsb, stream)
+    dec = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 8, 2, 64, 10, 500, 128, 0, 0.088, 10000.0,
+           ops.GQA_BF16, ops.GQA_F32, FAKE, 1 << 30, None]
+    def dcall(i, v):
+        a = list(dec); a[i] = v
+        return lib.gqa_append_decode_paged_rope(*a)
+    assert dcall(19, 0.0) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert dcall(13, 48) == ops.GQA_ERR_UNSUPPORTED
+    assert dcall(23, 0) == ops.GQA_ERR_WORKSPACE_TOO_SMALL
+    assert dcall(3, None) == ops.GQA_ERR_INVALID_ARGUMENT

@@ -252,3 +252,37 @@ def test_append_decode_paged_equals_two_calls(h_q, h_kv, ps):
     assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
     assert np.array_equal(o1, o2)
     assert np.all(np.isfinite(o1))
+
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(16, 2), (64, 2)], ids=["narrow_fused", "wide_two_launches"])
+def test_append_decode_paged_rope_equals_contiguous(h_q, h_kv):
+    """The rotating decode step over pages equals the same step over the contiguous
+    cache, bit for bit: same output, same rows written (pool pages vs cache rows)."""
+    import torch
+
+    B, d, ps, mp = 4, 128, 64, 20
+    lens = np.array([ps * mp, ps * 7 + 1, 300, 10], np.int32)
+    wp = lens - 1
+    print(f"case paged rope step h_q={h_q}", flush=True)
+    x = inputs.make_decode(B, h_q, h_kv, d, ps * mp, "bf16", 20500 + h_q, seq_lens=lens, poison=True)
+    kn = to_dev(inputs.normal(20500, "k_new", (B, h_kv, 1, d), "bf16"), "bf16")
+    vn = to_dev(inputs.normal(20500, "v_new", (B, h_kv, 1, d), "bf16"), "bf16")
+    kp, bt = _paginate(x["k_cache"], ps, 31)
+    vp, _ = _paginate(x["v_cache"], ps, 31)
+    q, sl, wpd = to_dev(x["q"], "bf16"), ints_dev(lens), ints_dev(wp)
+    kc, vc = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+    kpd, vpd, btd = to_dev(kp, "bf16"), to_dev(vp, "bf16"), ints_dev(bt)
+    o_c = ops.gqa_append_decode_rope(q, kc, vc, kn, vn, wpd, sl)
+    o_p = ops.gqa_append_decode_paged_rope(q, kpd, vpd, kn, vn, btd, wpd, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_p)
+    kc_h, kp_h = kc.cpu().view(torch.int16).numpy(), kpd.cpu().view(torch.int16).numpy()
+    for b in range(B):
+        pg, r = bt[b, wp[b] // ps], wp[b] % ps
+        assert np.array_equal(kp_h[pg, :, r], kc_h[b, :, wp[b]])
+    # the standalone paged rotating append writes the same rows
+    kp2, vp2 = to_dev(kp, "bf16"), to_dev(vp, "bf16")
+    ops.gqa_kv_append_paged_rope(kp2, vp2, kn, vn, btd, wpd)
+    torch.cuda.synchronize()
+    assert torch.equal(kp2.view(torch.int16), kpd.view(torch.int16)) and torch.equal(vp2.view(torch.int16), vpd.view(torch.int16))
