@@ -33,6 +33,7 @@
 // matrix phase opens with a few QK products whose K operands were read before
 // its barrier.  The ROPE instances rotate the workgroup's Q rows at their
 // positions (in LDS, once the first tile's loads are issued) before the loop.
+// O is written through LDS as whole 128-byte lines with the non-temporal hint.
 //
 // Layouts in LDS, both filled by 16-byte buffer loads that return zeros past the
 // last visible key (no per-load branches):
@@ -399,24 +400,59 @@ prefill_bf16_kernel(PrefillParams p) {
     p.lse[(size_t)(b * p.h_q + head) * p.S_q + qi] =
         l_tot > 0.f ? fmaf(__builtin_amdgcn_logf(l_tot), kLn2, m_run * p.scale) : -INFINITY;
   }
-  if (row_valid) {
-    const size_t obase = ((size_t)(b * p.h_q + head) * p.S_q + qi) * D;
+  // O leaves through LDS, so that a store instruction writes whole 128-byte lines of
+  // a few rows rather than 16-byte pieces of 32 rows, and with the non-temporal hint,
+  // so that the output does not sit dirty in L2 when the kernel ends.  The leading
+  // group uses the K stages (free after its last barrier), the trailing group the V
+  // stage its last phase does not read; each wave owns 32 rows of D + 16 bytes and
+  // passes its rows through in ESZ parts of D bytes.
+  {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int ESZ = OUT_BF16 ? 2 : 4;      // bytes per output value
+    constexpr int RS = D + 16;                 // LDS row stride, bytes
+    constexpr int DP = D / ESZ;                // d values per part
+    constexpr int CPR = D / 16;                // 16-byte chunks per row part
+    constexpr int RPI = 64 / CPR;              // rows per store instruction
+    static_assert(4 * 32 * RS <= 2 * L::K_STAGE, "leading rows fit the K stages");
+    static_assert(4 * 32 * RS <= L::V_STAGE, "trailing rows fit one V stage");
+    unsigned char* const wl = lds + (grp == 0 ? 0 : L::V_OFF + (n_tiles & 1) * L::V_STAGE) + (wave & 3) * 32 * RS;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int ps = 0; ps < ESZ; ++ps) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = db * 32 + 8 * j + 4 * h;
+      for (int u = ps * DP / 8; u < (ps + 1) * DP / 8; ++u) {
+        // unit u: d = 8 u + 4 h + e, held in oacc[u / 4][4 (u % 4) + e]
+        const int db = u / 4, j = u % 4;
+        const int off = (8 * u + 4 * h - ps * DP) * ESZ;
         const float o0 = oacc[db][4 * j] * inv, o1 = oacc[db][4 * j + 1] * inv;
         const float o2 = oacc[db][4 * j + 2] * inv, o3 = oacc[db][4 * j + 3] * inv;
         if constexpr (OUT_BF16) {
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           bf16x4 w;
           w[0] = (__bf16)o0; w[1] = (__bf16)o1; w[2] = (__bf16)o2; w[3] = (__bf16)o3;
-          *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + obase + d0) = w;
+          *reinterpret_cast<bf16x4*>(wl + col * RS + off) = w;
         } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.o) + obase + d0) = make_float4(o0, o1, o2, o3);
+          *reinterpret_cast<float4*>(wl + col * RS + off) = make_float4(o0, o1, o2, o3);
         }
       }
+      // the wave reads back what its own lanes wrote: order within the wave suffices
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int rw = it * RPI + lane / CPR;   // row within the wave
+        const int c = lane % CPR;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(wl + rw * RS + c * 16);
+        const int rho_ = wave * 32 + rw;
+        const int qi_ = qb * p.P + rho_ % p.P;
+        if (qi_ < p.S_q) {
+          const int head_ = g * p.r + hc * p.hp + rho_ / p.P;
+          unsigned char* orow = static_cast<unsigned char*>(p.o) + ((size_t)(b * p.h_q + head_) * p.S_q + qi_) * D * ESZ;
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(orow + ps * D + c * 16));
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
   }
 }
 
