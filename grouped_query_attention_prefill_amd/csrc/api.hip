@@ -41,7 +41,8 @@ bool bf16_rows_fit(int in_dtype, int rows, int d_h) {
 int check_ptrs(int in_dtype, int out_dtype, const void* q, const void* k, const void* v, const void* o) {
   if (!q || !k || !v || !o) return GQA_ERR_INVALID_ARGUMENT;
   const uintptr_t in_al = in_dtype == GQA_BF16 ? 16 : 4;
-  const uintptr_t out_al = in_dtype == GQA_BF16 ? (out_dtype == GQA_BF16 ? 8 : 16) : 4;
+  // the bf16 kernels write O as 16-byte vectors, whatever its element type
+  const uintptr_t out_al = in_dtype == GQA_BF16 ? 16 : 4;
   if (!aligned(q, in_al) || !aligned(k, in_al) || !aligned(v, in_al) || !aligned(o, out_al))
     return GQA_ERR_INVALID_ARGUMENT;
   return GQA_OK;

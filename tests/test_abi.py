@@ -80,6 +80,8 @@ def test_prefill_rejects_null_and_misaligned():
     assert lib.gqa_prefill(None, FAKE, FAKE, FAKE, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == ops.GQA_ERR_INVALID_ARGUMENT
     assert lib.gqa_prefill(FAKE + 2, FAKE, FAKE, FAKE, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == ops.GQA_ERR_INVALID_ARGUMENT
     assert lib.gqa_prefill(FAKE, FAKE, FAKE, FAKE + 4, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 0, None) == ops.GQA_ERR_INVALID_ARGUMENT
+    # a bf16 output needs 16-byte alignment too (it is written as 16-byte vectors)
+    assert lib.gqa_prefill(FAKE, FAKE, FAKE, FAKE + 8, 1, 4, 2, 8, 64, 1, None, 0.1, 1, 1, None) == ops.GQA_ERR_INVALID_ARGUMENT
 
 
 @needs_lib

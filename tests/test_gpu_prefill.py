@@ -122,6 +122,29 @@ def test_prefill_bf16_out_bf16():
     check_parity(got, _oracle(x, "bf16"), mode="bf16out", what="bf16 out")
 
 
+# The output leaves each wave through LDS in parts of d_h bytes per row, several rows
+# per store instruction; these shapes vary the rows' heads within a wave (r = 64, 128:
+# 2-4 positions per head), the part count (fp32 / bf16 output, d_h 64 / 128) and the
+# ragged last block.
+LAYOUT_CASES = [
+    # B, h_q, h_kv, T, d_h, output dtype
+    (1, 128, 1, 37, 128, "f32"),    # r=128: 128 heads x 2 positions per workgroup
+    (1, 64, 1, 45, 64, "bf16"),     # r=64, d_h 64, bf16 output
+    (1, 4, 4, 130, 64, "bf16"),     # MHA, d_h 64, bf16 output
+    (2, 8, 2, 97, 128, "bf16"),     # r=4, ragged last block, bf16 output
+    (1, 16, 2, 75, 64, "f32"),      # r=8: 8 heads x 32 positions, d_h 64
+]
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=lambda c: "B%d_hq%d_hkv%d_T%d_d%d_%s" % c)
+def test_prefill_bf16_output_layouts(case):
+    B, h_q, h_kv, T, d, od = case
+    print(f"case layout {case}", flush=True)
+    x = inputs.make_prefill(B, h_q, h_kv, d, T, "bf16", 8700 + T)
+    got = _run_prefill(x, "bf16", out_dtype=od)
+    check_parity(got, _oracle(x, "bf16"), mode="bf16out" if od == "bf16" else "bf16", what=str(case))
+
+
 def test_prefill_bf16_padding_and_poison():
     # keys past kv_lens are NaN: they must never reach the output
     B, h_q, h_kv, T, d = 3, 8, 2, 200, 128
@@ -168,6 +191,22 @@ def test_prefill_does_not_write_outside_output():
     torch.cuda.synchronize()
     g = guard.cpu().numpy()
     assert np.all(g[:1024] == 12345.0) and np.all(g[1024 + n:] == 12345.0)
+
+
+def test_prefill_bf16_out_does_not_write_outside_output():
+    import torch
+
+    # 100 positions: the last 64-position block holds 36 rows, the rest must stay untouched
+    x = inputs.make_prefill(1, 8, 2, 128, 100, "bf16", 8650)
+    q, k, v = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    n = 8 * 100 * 128
+    guard = torch.full((n + 2048,), 123.0, dtype=torch.bfloat16, device="cuda")
+    out = guard[1024:1024 + n].view(1, 8, 100, 128)
+    ops.gqa_prefill(q, k, v, out=out)
+    torch.cuda.synchronize()
+    g = guard.float().cpu().numpy()
+    assert np.all(g[:1024] == 123.0) and np.all(g[1024 + n:] == 123.0)
+    check_parity(out.float().cpu().numpy(), _oracle(x, "bf16"), mode="bf16out", what="guarded bf16 out")
 
 
 # ---------------------------------------------------------------- chunked / offset prefill
