@@ -38,13 +38,13 @@ bool bf16_rows_fit(int in_dtype, int rows, int d_h) {
   return in_dtype != GQA_BF16 || (long long)rows * d_h * 2 <= 0x7fffffffLL;
 }
 
-int check_ptrs(int in_dtype, int out_dtype, const void* q, const void* k, const void* v, const void* o) {
+// On the bf16 path every tensor, the output included, needs a 16-byte aligned base
+// (the prefill writes O as 16-byte vectors whatever its element type); the fp32 path
+// needs 4 bytes.
+int check_ptrs(int in_dtype, const void* q, const void* k, const void* v, const void* o) {
   if (!q || !k || !v || !o) return GQA_ERR_INVALID_ARGUMENT;
-  const uintptr_t in_al = in_dtype == GQA_BF16 ? 16 : 4;
-  // the bf16 kernels write O as 16-byte vectors, whatever its element type
-  const uintptr_t out_al = in_dtype == GQA_BF16 ? 16 : 4;
-  if (!aligned(q, in_al) || !aligned(k, in_al) || !aligned(v, in_al) || !aligned(o, out_al))
-    return GQA_ERR_INVALID_ARGUMENT;
+  const uintptr_t al = in_dtype == GQA_BF16 ? 16 : 4;
+  if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al)) return GQA_ERR_INVALID_ARGUMENT;
   return GQA_OK;
 }
 
@@ -75,7 +75,7 @@ static int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_
   int st = check_types(in_dtype, out_dtype, d_h);
   if (st != GQA_OK) return st;
   if (!bf16_rows_fit(in_dtype, T_cap, d_h)) return GQA_ERR_UNSUPPORTED;
-  st = check_ptrs(in_dtype, out_dtype, q, k_cache, v_cache, o);
+  st = check_ptrs(in_dtype, q, k_cache, v_cache, o);
   if (st != GQA_OK) return st;
   if ((kv_lens && !aligned(kv_lens, 4)) || (q_pos0 && !aligned(q_pos0, 4))) return GQA_ERR_INVALID_ARGUMENT;
   AttnArgs a;
@@ -119,7 +119,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   int st = check_types(in_dtype, out_dtype, d_h);
   if (st != GQA_OK) return st;
   if (!bf16_rows_fit(in_dtype, T, d_h)) return GQA_ERR_UNSUPPORTED;
-  st = check_ptrs(in_dtype, out_dtype, q, k, v, o);
+  st = check_ptrs(in_dtype, q, k, v, o);
   if (st != GQA_OK) return st;
   if (kv_lens && !aligned(kv_lens, 4)) return GQA_ERR_INVALID_ARGUMENT;
   if (lse && !aligned(lse, 4)) return GQA_ERR_INVALID_ARGUMENT;
@@ -235,7 +235,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return GQA_ERR_UNSUPPORTED;
   int st = check_types(in_dtype, out_dtype, d_h);
   if (st != GQA_OK) return st;
-  st = check_ptrs(in_dtype, out_dtype, q, k_cache, v_cache, o);
+  st = check_ptrs(in_dtype, q, k_cache, v_cache, o);
   if (st != GQA_OK) return st;
   if (!seq_lens || !aligned(seq_lens, 4) || (q_pos && !aligned(q_pos, 4))) return GQA_ERR_INVALID_ARGUMENT;
   const int eb = in_dtype == GQA_BF16 ? 2 : 4;
@@ -292,7 +292,7 @@ static int decode_paged_impl(const void* q, const void* k_pages, const void* v_p
   if (in_dtype != GQA_BF16 || page_size % 64 != 0) return GQA_ERR_UNSUPPORTED;
   int st = check_types(in_dtype, out_dtype, d_h);
   if (st != GQA_OK) return st;
-  st = check_ptrs(in_dtype, out_dtype, q, k_pages, v_pages, o);
+  st = check_ptrs(in_dtype, q, k_pages, v_pages, o);
   if (st != GQA_OK) return st;
   if (!block_table || !seq_lens || !aligned(block_table, 4) || !aligned(seq_lens, 4) || (q_pos && !aligned(q_pos, 4)))
     return GQA_ERR_INVALID_ARGUMENT;
