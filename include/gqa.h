@@ -339,8 +339,12 @@ int gqa_prefill_backward(const void* q, const void* k, const void* v, const void
  * pos0[b] + s (pos0 == NULL: s).  y may be x (in place); any other overlap is
  * undefined.  Use it on Q (H = h_q) before gqa_prefill / gqa_prefill_chunk /
  * gqa_decode, and on the prompt's K (H = h_kv) before it becomes the cache.
- * Arithmetic is fp32 with angles reduced in double precision; bf16 results are
- * rounded to nearest even.
+ * Angles: theta_i / 2 pi is passed to the kernels as a 64-bit fixed-point
+ * fraction of a turn (computed on the host), the integer product with p drops
+ * whole turns exactly, and the remaining fraction feeds the hardware sine and
+ * cosine; the rotation itself is fp32, and bf16 results are rounded to nearest
+ * even.  The calls that rotate inside the attention kernels use the same
+ * arithmetic and give bit-identical results.
  * Errors: INVALID_ARGUMENT for a size < 1, a NULL or misaligned pointer, a base
  * that is not finite or not > 1; UNSUPPORTED for an odd d_h, d_h > 256 or an
  * unknown dtype.
