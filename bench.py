@@ -324,8 +324,7 @@ def bench_rope(steps, warmup, flush_buf):
     qo, ko = torch.empty_like(q), torch.empty_like(k)
 
     def fn():
-        ops.gqa_rope(q, out=qo)
-        ops.gqa_rope(k, out=ko)
+        ops.gqa_rope_qk(q, k, q_out=qo, k_out=ko)
 
     log(f"[bench] timing rotary encoding of {w.name} Q and K")
     wall, per = time_calls(fn, steps, warmup, flush=lambda: flush_buf.sum())
@@ -345,7 +344,7 @@ def bench_rope(steps, warmup, flush_buf):
             "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
-            "kernels": "rope (Q) + rope (K)",
+            "kernels": "rope (Q and K, one launch)",
             "prefill_rope_fused": {"ms_per_call": round(fused_ms, 5),
                                    "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
                                    "rope_then_prefill_ms": round(sep_ms, 5)}}

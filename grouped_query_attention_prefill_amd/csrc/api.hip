@@ -441,6 +441,20 @@ int gqa_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, i
   return hip_status(gqa::launch_rope(x, y, pos0, B, H, S, d_h, base, eb, static_cast<hipStream_t>(stream)));
 }
 
+int gqa_rope_qk(const void* q, void* q_out, const void* k, void* k_out, const int32_t* pos0, int B,
+                int h_q, int h_kv, int S, int d_h, float base, int dtype, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || S < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (d_h < 2 || d_h % 2 != 0 || d_h / 2 > gqa::kRopeMaxHalf) return GQA_ERR_UNSUPPORTED;
+  if (!std::isfinite(base) || base <= 1.f) return GQA_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+  const int eb = dtype == GQA_BF16 ? 2 : 4;
+  if (!q || !q_out || !k || !k_out || !aligned(q, eb) || !aligned(q_out, eb) || !aligned(k, eb) ||
+      !aligned(k_out, eb) || (pos0 && !aligned(pos0, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  return hip_status(gqa::launch_rope_pair(q, q_out, h_q, k, k_out, h_kv, pos0, B, S, d_h, base, eb,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int gqa_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                        const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h, float base,
                        int dtype, void* stream) {

@@ -111,6 +111,9 @@ hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t s);
 
 // rotary encoding: head widths up to 2 * kRopeMaxHalf
 constexpr int kRopeMaxHalf = 128;
+// Two tensors (x: H heads, x2: H2 heads) rotated at the same positions in one launch.
+hipError_t launch_rope_pair(const void* x, void* y, int H, const void* x2, void* y2, int H2,
+                            const int32_t* pos0, int B, int S, int D, float base, int elem_bytes, hipStream_t s);
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, int D,
                        float base, int elem_bytes, hipStream_t s);
 hipError_t launch_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

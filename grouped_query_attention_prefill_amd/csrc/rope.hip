@@ -35,12 +35,28 @@ struct Vec<T, 1> { typedef T type; };
 // One thread per (row, VEC consecutive pairs).  Rows are (b, h, s) of a (B, H, S, d)
 // tensor; row s of sequence b sits at position pos0[b] + s.  With VEC > 1 both halves
 // of the pairs move as 16-byte vectors.
+// One launch may rotate two tensors of the same rows' positions (Q and K): chunk
+// indices past the first tensor's fall to the second.
+struct RopeSeg {
+  const void* x;
+  void* y;
+  int H;
+  long long n_chunks;
+};
+
 template <typename T, int VEC>
 __global__ void __launch_bounds__(256)
-rope_kernel(const T* x, T* y, const int32_t* pos0, int H, int S, int half, long long n_chunks, RopeFreq f) {
+rope_kernel(RopeSeg a, RopeSeg a2, const int32_t* pos0, int S, int half, RopeFreq f) {
   typedef typename Vec<T, VEC>::type V;
-  const long long cidx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (cidx >= n_chunks) return;
+  long long cidx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const bool second = cidx >= a.n_chunks;
+  if (second) {
+    cidx -= a.n_chunks;
+    if (cidx >= a2.n_chunks) return;
+  }
+  const T* x = static_cast<const T*>(second ? a2.x : a.x);
+  T* y = static_cast<T*>(second ? a2.y : a.y);
+  const int H = second ? a2.H : a.H;
   const int chunks = half / VEC;
   const long long row = cidx / chunks;
   const int i0 = (int)(cidx - row * chunks) * VEC;
@@ -101,29 +117,31 @@ kv_append_rope_kernel(T* kc, T* vc, const T* kn, const T* vn, const int32_t* wri
 
 }  // namespace
 
-hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, int D,
-                       float base, int elem_bytes, hipStream_t s) {
+hipError_t launch_rope_pair(const void* x, void* y, int H, const void* x2, void* y2, int H2,
+                            const int32_t* pos0, int B, int S, int D, float base, int elem_bytes, hipStream_t s) {
   const int half = D / 2;
-  const long long n_rows = (long long)B * H * S;
   const RopeFreq f = make_rope_freq(D, base);
-  const bool al16 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+  auto al = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+  const bool al16 = al(x) && al(y) && (H2 == 0 || (al(x2) && al(y2)));
   const int vec = !al16 ? 1 : (elem_bytes == 4 ? (half % 4 == 0 ? 4 : 1) : (half % 8 == 0 ? 8 : 1));
-  const long long n_chunks = n_rows * (half / vec);
-  const long long blocks = (n_chunks + 255) / 256;
+  const RopeSeg a{x, y, H, (long long)B * H * S * (half / vec)};
+  const RopeSeg a2{x2, y2, H2, (long long)B * H2 * S * (half / vec)};
+  const long long blocks = (a.n_chunks + a2.n_chunks + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
   if (elem_bytes == 4) {
-    const float* xi = static_cast<const float*>(x);
-    float* yo = static_cast<float*>(y);
-    if (vec == 4) hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
-    else hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
+    if (vec == 4) hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, 0, s, a, a2, pos0, S, half, f);
+    else hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, 0, s, a, a2, pos0, S, half, f);
   } else {
-    const uint16_t* xi = static_cast<const uint16_t*>(x);
-    uint16_t* yo = static_cast<uint16_t*>(y);
-    if (vec == 8) hipLaunchKernelGGL((rope_kernel<uint16_t, 8>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
-    else hipLaunchKernelGGL((rope_kernel<uint16_t, 1>), grid, block, 0, s, xi, yo, pos0, H, S, half, n_chunks, f);
+    if (vec == 8) hipLaunchKernelGGL((rope_kernel<uint16_t, 8>), grid, block, 0, s, a, a2, pos0, S, half, f);
+    else hipLaunchKernelGGL((rope_kernel<uint16_t, 1>), grid, block, 0, s, a, a2, pos0, S, half, f);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, int D,
+                       float base, int elem_bytes, hipStream_t s) {
+  return launch_rope_pair(x, y, H, nullptr, nullptr, 0, pos0, B, S, D, base, elem_bytes, s);
 }
 
 namespace {

@@ -51,6 +51,7 @@ SIGNATURES = {
     "gqa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "gqa_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_rope": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "gqa_rope_qk": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_kv_append_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_prefill_lse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P]),
     "gqa_prefill_backward_workspace_bytes": (_S, [_I, _I, _I]),
@@ -511,6 +512,31 @@ def gqa_rope(x, *, pos0=None, base: float = ROPE_BASE, out=None):
     _launch(x.device, (("out", out),), load_library().gqa_rope,
             _ptr(x), _ptr(out), _ptr(pos0), B, H, S, d_h, float(base), _dtype_code(x))
     return out
+
+
+def gqa_rope_qk(q, k, *, pos0=None, base: float = ROPE_BASE, q_out=None, k_out=None):
+    """gqa_rope of q (B, h_q, S, d_h) and k (B, h_kv, S, d_h) at the same positions, one launch.
+
+    Returns (q_out, k_out) (new tensors when None; pass q_out=q, k_out=k to rotate in place).
+    """
+    torch = _torch()
+    _dev_tensor(q, "q", 4)
+    _dev_tensor(k, "k", 4)
+    B, h_q, S, d_h = q.shape
+    _require(k.dim() == 4 and k.shape[0] == B and k.shape[2:] == q.shape[2:] and k.dtype == q.dtype,
+             "k must be (B, h_kv, S, d_h) of q's dtype")
+    h_kv = k.shape[1]
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _dev_tensor(q_out, "q_out", 4)
+    _dev_tensor(k_out, "k_out", 4)
+    _require(q_out.shape == q.shape and q_out.dtype == q.dtype, "q_out must match q")
+    _require(k_out.shape == k.shape and k_out.dtype == k.dtype, "k_out must match k")
+    pos0 = _int_vec(pos0, "pos0", B, q.device)
+    _launch(q.device, (("q_out", q_out), ("k", k), ("k_out", k_out)), load_library().gqa_rope_qk,
+            _ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out), _ptr(pos0), B, h_q, h_kv, S, d_h, float(base),
+            _dtype_code(q))
+    return q_out, k_out
 
 
 def gqa_kv_append_paged_rope(k_pages, v_pages, k_new, v_new, block_table, write_pos, *, base: float = ROPE_BASE):

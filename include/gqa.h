@@ -353,6 +353,17 @@ int gqa_rope(const void* x, void* y, const int32_t* pos0, int B, int H, int S, i
              int dtype, void* stream);
 
 /*
+ * gqa_rope_qk: gqa_rope of q (B, h_q, S, d_h) into q_out and of k (B, h_kv, S,
+ * d_h) into k_out, both at positions pos0[b] + s, in one launch (the rotations
+ * named above for the query heads and the kept key heads).  Results are
+ * bit-identical to two gqa_rope calls.  q_out may be q and k_out may be k (in
+ * place); any other overlap among the four tensors is undefined.
+ * Errors: as gqa_rope, for each tensor.
+ */
+int gqa_rope_qk(const void* q, void* q_out, const void* k, void* k_out, const int32_t* pos0, int B,
+                int h_q, int h_kv, int S, int d_h, float base, int dtype, void* stream);
+
+/*
  * gqa_kv_append with the key rotated at its own position write_pos[b] on the way
  * into the cache (values are copied unchanged).  Rows already in the cache are
  * never touched: a cache that other readers share stays read-only to them

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
               "gqa_kv_append", "gqa_status_string", "gqa_decode_paged", "gqa_kv_append_paged",
-              "gqa_rope", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
+              "gqa_rope", "gqa_rope_qk", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
               "gqa_prefill_backward_workspace_bytes", "gqa_append_decode", "gqa_append_decode_paged",
               "gqa_prefill_rope", "gqa_append_decode_rope", "gqa_prefill_chunk_rope", "gqa_kv_append_paged_rope",
               "gqa_append_decode_paged_rope"):
@@ -152,6 +152,20 @@ def test_rope_validation():
     assert call(y=FAKE + 1) == ops.GQA_ERR_INVALID_ARGUMENT       # misaligned bf16
     assert call(dtype=7) == ops.GQA_ERR_UNSUPPORTED
     assert call(x=FAKE + 2, dtype=ops.GQA_F32) == ops.GQA_ERR_INVALID_ARGUMENT
+    ok2 = (FAKE, FAKE, FAKE, FAKE, None, 2, 8, 2, 16, 128, 10000.0, ops.GQA_BF16, None)
+    def call2(**kw):
+        names = ["q", "q_out", "k", "k_out", "pos0", "B", "h_q", "h_kv", "S", "d", "base", "dtype", "stream"]
+        a = list(ok2)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.gqa_rope_qk(*a)
+    assert call2(d=127) == ops.GQA_ERR_UNSUPPORTED
+    assert call2(base=0.5) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call2(h_kv=0) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call2(k=None) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call2(k_out=FAKE + 1) == ops.GQA_ERR_INVALID_ARGUMENT   # misaligned bf16
+    assert call2(pos0=FAKE + 2) == ops.GQA_ERR_INVALID_ARGUMENT
+    assert call2(dtype=7) == ops.GQA_ERR_UNSUPPORTED
     assert lib.gqa_kv_append_rope(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 8, 64, 10000.0, 1, None) == \
         ops.GQA_ERR_INVALID_ARGUMENT
     assert lib.gqa_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 63, 10000.0, 1, None) == \

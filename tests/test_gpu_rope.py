@@ -79,6 +79,34 @@ def test_rope_in_place_equals_out_of_place():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("dt,h_q,h_kv,S,d,offset", [("bf16", 32, 8, 300, 128, 0), ("f32", 8, 2, 77, 64, 0),
+                                                  ("bf16", 6, 3, 50, 64, 1), ("bf16", 4, 1, 33, 18, 0)],
+                         ids=["bf16_vec8", "f32_vec4", "bf16_misaligned", "bf16_d18"])
+def test_rope_qk_one_launch_equals_two_calls(dt, h_q, h_kv, S, d, offset):
+    import torch
+
+    print(f"case rope_qk {dt} {h_q} {h_kv} {S} {d} {offset}", flush=True)
+    xq = inputs.normal(13300 + d, "q", (2, h_q, S, d), dt)
+    xk = inputs.normal(13300 + d, "k", (2, h_kv, S, d), dt)
+    q, k = to_dev(xq, dt), to_dev(xk, dt)
+    if offset:   # one element into a larger buffer: not 16-byte aligned, so the element-wise path
+        qb = torch.empty(q.numel() + offset, dtype=q.dtype, device="cuda")
+        qb[offset:] = q.flatten()
+        q = qb[offset:].view(q.shape)
+    pos = ints_dev([5, 9000])
+    qa, ka = ops.gqa_rope_qk(q, k, pos0=pos)
+    qb_, kb_ = ops.gqa_rope(q, pos0=pos), ops.gqa_rope(k, pos0=pos)
+    torch.cuda.synchronize()
+    iv = (lambda t: t.view(torch.int16)) if dt == "bf16" else (lambda t: t.view(torch.int32))
+    assert torch.equal(iv(qa), iv(qb_)) and torch.equal(iv(ka), iv(kb_))
+    want = oracle.rope(f64(xk, dt), np.array([5, 9000])[:, None, None] + np.arange(S)[None, None, :])
+    _check_rope(to_host64(ka), want, dt, "rope_qk k", x=f64(xk, dt))
+    # in place
+    ops.gqa_rope_qk(q, k, pos0=pos, q_out=q, k_out=k)
+    torch.cuda.synchronize()
+    assert torch.equal(iv(q), iv(qb_)) and torch.equal(iv(k), iv(kb_))
+
+
 @pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
 def test_kv_append_rope(dt, d):
     import torch
