@@ -83,7 +83,9 @@ static int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_
   a.kv_lens = kv_lens; a.q_pos0 = q_pos0;
   a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.S_q = S_q; a.T_cap = T_cap; a.D = d_h;
   a.causal = mask == GQA_MASK_CAUSAL ? 1 : 0;
-  a.q_pos_from_end = 1;
+  // default positions: the newest S_q positions of each history, except when the
+  // chunk spans the whole capacity, which is a prefill (row i at position i)
+  a.q_pos_from_end = S_q == T_cap ? 0 : 1;
   a.scale = scale;
   a.out_bf16 = out_dtype == GQA_BF16 ? 1 : 0;
   a.rope_base = rope_base;

@@ -8,8 +8,8 @@ Recipe (the same for every workload):
   * numpy PCG64 streams keyed by ``SeedSequence(seed, spawn_key=(tensor, row))``:
     one independent stream per tensor and per batch row, so rows can be drawn
     in parallel threads and any row can be regenerated on its own;
-    tensor ids: Q 0, K 1, V 2, appended K 3, appended V 4, lengths 5 (one stream),
-    output gradient dO 6;
+    tensor ids: Q 0, K 1, V 2, appended K 3, appended V 4, output gradient dO 6;
+  * ragged lengths come first, from ``Generator(PCG64(seed))`` itself;
   * values are ``standard_normal(dtype=float32)``, i.e. N(0, 1);
   * bf16 tensors are those float32 draws rounded to bf16, round-to-nearest-even;
     both sides see exactly those bf16 values (the oracle widens them to float64
@@ -98,7 +98,11 @@ def normal_row(seed: int, tensor: str, row: int, shape_tail, dtype: str) -> np.n
 
 
 def ragged_lengths(seed: int, B: int, lo: int = 1, hi: int = 32768) -> np.ndarray:
-    return rng_for(seed, TENSOR_IDS["lengths"]).integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    """B history lengths uniform on [lo, hi], both ends inclusive, drawn first and
+    from a plain ``Generator(PCG64(seed))`` (the tensors keep their keyed streams).
+    For seed 1953, B = 32 the histories sum to 543,025 - 32 rows (543,025 with the
+    appended token)."""
+    return np.random.Generator(np.random.PCG64(seed)).integers(lo, hi, size=B, endpoint=True).astype(np.int32)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -158,10 +158,16 @@ def _launch(device, tensors, fn, *args) -> None:
 
 
 def _out_code(in_code: int, out_dtype) -> int:
+    """Output dtype code; only float32 and bfloat16 outputs exist (a caller-supplied
+    ``out`` of any other dtype would receive the wrong element size)."""
     if out_dtype is None:
         return GQA_F32
     torch = _torch()
-    return GQA_F32 if out_dtype == torch.float32 else GQA_BF16
+    if out_dtype == torch.float32:
+        return GQA_F32
+    if out_dtype == torch.bfloat16:
+        return GQA_BF16
+    raise TypeError(f"output dtype must be torch.float32 or torch.bfloat16, got {out_dtype}")
 
 
 # ------------------------------------------------------------------ entry points

@@ -101,8 +101,11 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o,
  * packed row keeps its own causal position; [Ch09] 09.2: absolute positions).
  * Key j is visible to query i iff j < kv_lens[b] and (mask == NONE or
  * j <= q_pos0[b] + i).  With q_pos0 = 0, S_q = T_cap = T and kv_lens = T this
- * is gqa_prefill.  q_pos0 == NULL means kv_lens[b] - S_q (the newest S_q
- * positions); kv_lens == NULL means T_cap.
+ * is gqa_prefill.  q_pos0 == NULL means kv_lens[b] - S_q (the chunk is the
+ * newest S_q positions of the history) when S_q != T_cap, and 0 when S_q ==
+ * T_cap: a chunk as long as the cache is a prefill, row i at position i, and
+ * kv_lens then masks keys only, exactly as in gqa_prefill.  kv_lens == NULL
+ * means T_cap.
  *
  *   q (B, h_q, S_q, d_h)  k_cache, v_cache (B, h_kv, T_cap, d_h)  o (B, h_q, S_q, d_h)
  * Errors: as gqa_prefill.
@@ -242,7 +245,8 @@ int gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
 
 /*
  * gqa_prefill_chunk with query row i of sequence b rotated at its absolute
- * position q_pos0[b] + i (q_pos0 == NULL: kv_lens[b] - S_q + i, as there).
+ * position q_pos0[b] + i (q_pos0 == NULL: the default positions of
+ * gqa_prefill_chunk).
  * Supported and errors as gqa_prefill_rope; otherwise as gqa_prefill_chunk.
  */
 int gqa_prefill_chunk_rope(const void* q, const void* k_cache, const void* v_cache, void* o,

@@ -2,8 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-This is the algorithm of [EffSeq] 在线 softmax, taken in the page's order and
-notation and written from its description:
+This is the algorithm of [EffSeq] 在线 softmax in the page's notation, built
+here as a fold: every block's own state is merged into the running one.  The
+page's description:
 
   state after the positions J already read:
       m = max_{j in J} s_j,   l = sum_{j in J} e^{s_j - m},   u = sum_{j in J} e^{s_j - m} v_j
@@ -32,44 +33,55 @@ def _empty_state(d: int):
     return (-np.inf, 0.0, np.zeros(d, dtype=np.float64))
 
 
+def block_state(scores, values):
+    """State (m, l, u) of one block of keys taken on its own.
+
+    m is the largest visible score of the block, l = sum_j e^{s_j - m} and
+    u = sum_j e^{s_j - m} v_j over its visible keys; a block whose keys are all
+    masked is the empty state (-inf, 0, 0), so it leaves any state it is merged
+    into unchanged ([EffSeq] 在线 softmax: fully masked blocks are skipped).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    v = np.asarray(values, dtype=np.float64)
+    live = np.isfinite(s)
+    if not live.any():
+        return _empty_state(v.shape[1])
+    m = float(np.max(s[live]))
+    w = np.exp(s[live] - m)
+    return (m, float(np.sum(w)), w @ v[live])
+
+
 def online_states(scores, values, block: int):
-    """Yield the state (m, l, u) after each block of ``block`` keys.
+    """Yield the running state (m, l, u) after each block of ``block`` keys.
 
     scores: (T,) scaled and masked scores (masked entries are -inf).
     values: (T, d) value vectors.
-    Blocks with no visible key leave the state unchanged (and still yield it).
+    The running state starts empty and takes each block's own state through
+    ``merge_states``: both move to the common base m' = max(m, m_hat), which is
+    the page's update l' = e^{m - m'} l + sum_I e^{s_j - m'} (and the same for u),
+    since sum_I e^{s_j - m'} = e^{m_hat - m'} sum_I e^{s_j - m_hat}.
     """
     s_all = np.asarray(scores, dtype=np.float64)
     v_all = np.asarray(values, dtype=np.float64)
     if s_all.ndim != 1 or v_all.ndim != 2 or v_all.shape[0] != s_all.shape[0]:
-        raise ValueError("scores must be (T,) and values (T, d)")
+        raise ValueError("expected scores of shape (T,) and values of shape (T, d)")
     if block < 1:
-        raise ValueError("block must be >= 1")
-    if not np.all(np.isfinite(s_all) | np.isneginf(s_all)):
-        raise ValueError("scores must be finite or -inf")
+        raise ValueError("the block length is at least one key")
+    if np.any(np.isnan(s_all) | (s_all == np.inf)):
+        raise ValueError("a score is NaN or +inf; masked keys carry -inf")
     if not np.all(np.isfinite(v_all)):
-        raise ValueError("values must be finite")
-    m, l, u = _empty_state(v_all.shape[1])
+        raise ValueError("a value vector holds NaN or inf")
+    state = _empty_state(v_all.shape[1])
     for start in range(0, s_all.shape[0], block):
-        s = s_all[start:start + block]
-        v = v_all[start:start + block]
-        seen = ~np.isneginf(s)
-        if seen.any():
-            s, v = s[seen], v[seen]
-            m_new = max(m, float(np.max(s)))
-            carry = np.exp(m - m_new)          # e^{m - m'}; 0 while nothing has been read
-            w = np.exp(s - m_new)              # e^{s_j - m'} for j in the new block
-            l = carry * l + float(np.sum(w))
-            u = carry * u + w @ v
-            m = m_new
-        yield (m, l, u.copy())
+        state = merge_states(state, block_state(s_all[start:start + block], v_all[start:start + block]))
+        yield (state[0], state[1], np.array(state[2], dtype=np.float64))
 
 
 def finish_state(state) -> np.ndarray:
-    """o = u / l; a state that saw no visible key has no output."""
+    """o = u / l; a state built from no visible key has no output."""
     m, l, u = state
     if l == 0.0:
-        raise ValueError("query has no visible key")
+        raise ValueError("no key is visible to this query row, so its output is undefined")
     return u / l
 
 
@@ -79,7 +91,7 @@ def online_attention_row(scores, values, block: int = 2) -> np.ndarray:
     for state in online_states(scores, values, block):
         pass
     if state is None:
-        raise ValueError("query has no visible key")
+        raise ValueError("no key is visible to this query row, so its output is undefined")
     return finish_state(state)
 
 

@@ -58,10 +58,12 @@ def default_scale(d_h: int) -> float:
 def default_q_pos(B: int, S_q: int, T_k: int, kv_len: np.ndarray) -> np.ndarray:
     """Absolute position of every query row when the caller gives none.
 
-    Prefill (S_q == T_k): query i sits at position i.  Otherwise the S_q queries
+    Prefill (S_q == T_k): query i sits at position i, whatever kv_len (the
+    padding mask removes keys, not query positions).  Otherwise the S_q queries
     are the newest S_q positions of the visible history: kv_len[b] - S_q + i
     ([MhaMqaGqa] parameter table: T counts the visible history including the
-    current position; [Ch09] 09.2: absolute query position in cached decoding).
+    current position; [Ch09] 09.2: a cached query carries its absolute
+    position, the current-position pointer, not its index in the chunk).
     """
     pos = np.empty((B, S_q), dtype=np.int64)
     for b in range(B):
@@ -92,7 +94,7 @@ def softmax_rows(S: np.ndarray) -> np.ndarray:
     ([EffSeq] 在线 softmax, paragraph on subtracting the maximum).
     """
     if not np.all(np.any(np.isfinite(S), axis=1)):
-        raise ValueError("query has no visible key")
+        raise ValueError("a query row sees no key, so its softmax is undefined")
     m = np.max(S, axis=1, keepdims=True)
     E = np.exp(S - m)
     return E / np.sum(E, axis=1, keepdims=True)

@@ -56,3 +56,21 @@ def check_parity(got: np.ndarray, want: np.ndarray, *, mode: str, what: str = ""
     assert err.mean() <= BF16_MEAN_ABS + (bf16_half_ulp(want).mean() if mode == "bf16out" else 0.0), \
         f"{what}: mean-abs {err.mean():.3g}"
     return err.max(), err.mean()
+
+
+def host_workers() -> int:
+    import os
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def parallel_map(fn, items):
+    """fn over items in host threads (numpy releases the GIL in the oracle's array work)."""
+    import concurrent.futures
+
+    with concurrent.futures.ThreadPoolExecutor(host_workers()) as ex:
+        return list(ex.map(fn, items))

@@ -336,3 +336,39 @@ def test_paged_rope_validation():
     assert dcall(13, 48) == ops.GQA_ERR_UNSUPPORTED
     assert dcall(23, 0) == ops.GQA_ERR_WORKSPACE_TOO_SMALL
     assert dcall(3, None) == ops.GQA_ERR_INVALID_ARGUMENT
+
+
+def test_binding_rejects_other_output_dtypes_before_any_call(monkeypatch):
+    """Only float32 and bfloat16 outputs exist: a caller-supplied ``out`` (or an
+    ``out_dtype``) of any other dtype raises TypeError before the library is called
+    (an int8 ``out`` would otherwise receive 2-byte values into 1-byte elements)."""
+    torch = pytest.importorskip("torch")
+    calls = []
+
+    class _Stub:
+        def __getattr__(self, name):
+            def fn(*a):
+                calls.append(name)
+                return 0
+            return fn
+
+    # host tensors stand in for device tensors: the checks under test come first
+    monkeypatch.setattr(ops, "_dev_tensor", lambda *a, **k: None)
+    monkeypatch.setattr(ops, "load_library", lambda *a, **k: _Stub())
+    bf = torch.bfloat16
+    q4, kv4 = torch.zeros(1, 4, 8, 64, dtype=bf), torch.zeros(1, 2, 8, 64, dtype=bf)
+    qd = torch.zeros(1, 4, 1, 64, dtype=bf)
+    for bad in (torch.float16, torch.int8, torch.uint8, torch.bool, torch.float64):
+        with pytest.raises(TypeError):
+            ops.gqa_prefill(q4, kv4, kv4, out=torch.zeros(1, 4, 8, 64, dtype=bad))
+        with pytest.raises(TypeError):
+            ops.gqa_prefill(q4, kv4, kv4, out_dtype=bad)
+        with pytest.raises(TypeError):
+            ops.gqa_prefill_chunk(q4, kv4, kv4, out=torch.zeros(1, 4, 8, 64, dtype=bad))
+        with pytest.raises(TypeError):
+            ops.gqa_decode(qd, kv4, kv4, torch.full((1,), 8, dtype=torch.int32),
+                           out=torch.zeros(1, 4, 1, 64, dtype=bad))
+    assert calls == []
+    assert ops._out_code(ops.GQA_BF16, torch.float32) == ops.GQA_F32
+    assert ops._out_code(ops.GQA_BF16, torch.bfloat16) == ops.GQA_BF16
+

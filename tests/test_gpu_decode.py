@@ -262,3 +262,51 @@ def test_append_decode_ragged_parity():
                           q_pos=x["q_pos"])
     check_parity(to_host64(o), want, mode="bf16", what="fused append+decode")
     assert np.array_equal(kd.cpu().view(torch.int16).numpy(), k.view(np.int16))
+
+
+# Kernel paths the shapes below reach (split plan for the bf16 path):
+#   r > 16, T_cap <= 256        -> wide kernel, one split, output written directly
+#   r > 16, T_cap = 3000        -> wide kernel, 12 splits, batched merge
+#   r = 16, T_cap = 9000        -> 16x16 kernel, 36 splits, batched merge
+#   r = 4,  T_cap = 1500        -> 16x16 kernel, 6 splits, plain merge
+PATH_CASES = [
+    # B, h_q, h_kv, T_cap, d_h, lens
+    (2, 32, 1, 200, 128, [200, 77]),
+    (2, 32, 1, 200, 64, [200, 3]),
+    (2, 64, 2, 3000, 64, [3000, 1999]),
+    (2, 32, 1, 3000, 128, [3000, 2048]),
+    (1, 16, 1, 9000, 128, [9000]),
+    (2, 8, 2, 1500, 64, [1500, 700]),
+]
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: "B%d_hq%d_hkv%d_T%d_d%d" % c[:5])
+def test_decode_kernel_paths_and_output_dtypes(case, out_dtype):
+    """Every decode kernel path (wide kernel at d_h 64 and 128, direct write, plain
+    and batched merge) with fp32 and bf16 output, against the oracle."""
+    B, h_q, h_kv, T_cap, d, lens = case
+    print(f"case decode path {case[:5]} out {out_dtype}", flush=True)
+    x = inputs.make_decode(B, h_q, h_kv, d, T_cap, "bf16", 12000 + T_cap + d, seq_lens=lens, poison=True)
+    got = _decode(x, "bf16", out_dtype=out_dtype)
+    check_parity(got, _oracle_decode(x, "bf16"), mode="bf16out" if out_dtype == "bf16" else "bf16",
+                 what=f"{case[:5]} {out_dtype}")
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(16, 4), (64, 2)], ids=["r4_16x16", "r32_wide"])
+def test_decode_max_seq_len_truncates_visibility(h_q, h_kv):
+    """max_seq_len below a sequence's length hides the keys at and past it: the
+    visible keys are j < min(seq_lens[b], q_pos[b] + 1, max_seq_len), checked
+    against the oracle with the history cut there."""
+    lens = np.array([5000, 4000, 3000, 900], np.int32)
+    msl = 3500
+    print(f"case decode max_seq_len {msl} h_q={h_q} h_kv={h_kv}", flush=True)
+    x = inputs.make_decode(len(lens), h_q, h_kv, 128, 5000, "bf16", 12500 + h_q, seq_lens=lens, poison=True)
+    got = _decode(x, "bf16", max_seq_len=msl)
+    want = []
+    for b in range(len(lens)):
+        L = int(min(lens[b], msl))
+        want.append(oracle.attention(f64(x["q"][b:b + 1], "bf16"), f64(x["k_cache"][b:b + 1, :, :L], "bf16"),
+                                     f64(x["v_cache"][b:b + 1, :, :L], "bf16"), causal=True,
+                                     q_pos=np.array([[lens[b] - 1]]), kv_len=np.array([L]))[0])
+    check_parity(got, np.stack(want), mode="bf16", what=f"max_seq_len {msl}")

@@ -244,3 +244,26 @@ def test_prefill_chunk(case):
     torch.cuda.synchronize()
     want2 = oracle.attention(f64(q, dt), f64(k, dt), f64(v, dt), causal=True, kv_len=lens)
     check_parity(to_host64(o2), want2, mode=mode, what=str(case) + " default positions")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_chunk_full_capacity_default_positions(dt):
+    """A chunk as long as the cache (S_q == T_cap) with shorter kv_lens and no
+    explicit positions is a prefill: row i sits at position i and kv_lens masks
+    keys only, as the oracle's default positions say ([Ch09] 09.2: positions are
+    absolute).  Matches gqa_prefill with the same kv_lens."""
+    import torch
+
+    B, h_q, h_kv, T, d = 3, 8, 2, 300, 128 if dt == "bf16" else 24
+    print(f"case chunk S_q == T_cap {dt}", flush=True)
+    q = inputs.normal(9700, "q", (B, h_q, T, d), dt)
+    k = inputs.normal(9700, "k", (B, h_kv, T, d), dt)
+    v = inputs.normal(9700, "v", (B, h_kv, T, d), dt)
+    lens = np.array([300, 173, 64], np.int32)
+    o = ops.gqa_prefill_chunk(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), kv_lens=ints_dev(lens))
+    p = ops.gqa_prefill(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), kv_lens=ints_dev(lens))
+    torch.cuda.synchronize()
+    got = to_host64(o)
+    want = oracle.attention(f64(q, dt), f64(k, dt), f64(v, dt), causal=True, kv_len=lens)
+    check_parity(got, want, mode="f32" if dt == "f32" else "bf16", what=f"chunk S_q == T_cap {dt}")
+    assert np.array_equal(got, to_host64(p)), "the full-capacity chunk must equal gqa_prefill"

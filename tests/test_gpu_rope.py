@@ -261,11 +261,19 @@ def test_prefill_chunk_rope_equals_rope_then_chunk(explicit_pos):
     lens = np.array([1000, 640, 101], np.int32)
     pos0 = np.array([900, 200, 1], np.int32) if explicit_pos else lens - S_q
     qp = ints_dev(pos0) if explicit_pos else None
+    q_host = inputs.normal(13700, "q", (B, h_q, S_q, d), "bf16")
     o_sep = ops.gqa_prefill_chunk(ops.gqa_rope(q, pos0=ints_dev(pos0)), kc, vc, kv_lens=ints_dev(lens), q_pos0=qp)
     o_fused = ops.gqa_prefill_chunk_rope(q, kc, vc, kv_lens=ints_dev(lens), q_pos0=qp)
     torch.cuda.synchronize()
     assert torch.equal(o_fused, o_sep)
     assert bool(torch.isfinite(o_fused).all())
+    # and against the oracle: keys rotated at 0..T_cap-1, query row i at pos0[b] + i,
+    # both rounded to bf16 as the kernels' operands are
+    qpos = pos0[:, None].astype(np.int64) + np.arange(S_q)[None]
+    kr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(x["k_cache"], "bf16"), np.arange(T_cap)))).astype(np.float64)
+    qr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(q_host, "bf16"), qpos[:, None, :]))).astype(np.float64)
+    want = oracle.attention(qr, kr, f64(x["v_cache"], "bf16"), causal=True, q_pos=qpos, kv_len=lens)
+    check_parity(to_host64(o_fused), want, mode="bf16", what=f"chunk rope explicit={explicit_pos}")
 
 
 @pytest.mark.parametrize("d", [128, 64])
@@ -292,3 +300,21 @@ def test_append_decode_rope_edge_positions(d):
     torch.cuda.synchronize()
     assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)) and torch.equal(v1.view(torch.int16), v2.view(torch.int16))
     assert torch.equal(o1, o2)
+    # and against the oracle: the cache rows as given, except an appended row inside the
+    # visible range, which holds the new key rotated at its write position; the query
+    # rotated at its position lens[b] - 1
+    kn_h = inputs.normal(13800 + d, "k_new", (B, h_kv, 1, d), "bf16")
+    vn_h = inputs.normal(13800 + d, "v_new", (B, h_kv, 1, d), "bf16")
+    got = to_host64(o2)
+    for b in range(B):
+        L = int(lens[b])
+        k = f64(x["k_cache"][b:b + 1, :, :L], "bf16").copy()
+        v = f64(x["v_cache"][b:b + 1, :, :L], "bf16").copy()
+        if 0 <= wp[b] < L:
+            rot = oracle.rope(f64(kn_h[b:b + 1], "bf16"), np.array([[wp[b]]]))
+            k[0, :, wp[b]] = inputs.bf16_bits_to_f32(_bf16_round(rot)).astype(np.float64)[0, :, 0]
+            v[0, :, wp[b]] = f64(vn_h[b, :, 0], "bf16")
+        qr = inputs.bf16_bits_to_f32(_bf16_round(oracle.rope(f64(x["q"][b:b + 1], "bf16"),
+                                                             np.array([[L - 1]])))).astype(np.float64)
+        want = oracle.attention(qr, k, v, causal=True, q_pos=np.array([[L - 1]]), kv_len=np.array([L]))
+        check_parity(got[b:b + 1], want, mode="bf16", what=f"rope decode edges b={b} wp={wp[b]}")

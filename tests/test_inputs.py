@@ -62,3 +62,17 @@ def test_normal_row_matches_full_draw():
     full = inputs.normal(77, "k", (3, 2, 5, 4), "bf16")
     for b in range(3):
         assert np.array_equal(inputs.normal_row(77, "k", b, (2, 5, 4), "bf16"), full[b])
+
+
+def test_ragged_workload_lengths_follow_the_plain_generator():
+    """History lengths of the ragged workload: Generator(PCG64(1953)).integers(1, 32768,
+    32, endpoint=True), drawn before any tensor; with the appended token the 32
+    sequences hold 543,025 rows, i.e. 2,224,230,400 bytes of bf16 K and V at
+    h_kv = 8, d_h = 128."""
+    w = inputs.WORKLOADS["ragged_append_decode_B32"]
+    h = inputs.ragged_lengths(w.seed, w.B, 1, w.hist_hi)
+    want = np.random.Generator(np.random.PCG64(1953)).integers(1, 32768, 32, endpoint=True)
+    assert np.array_equal(h, want)
+    assert int((h + 1).sum()) == 543_025
+    assert int((h + 1).sum()) * 2 * w.h_kv * w.d_h * 2 == 2_224_230_400
+    assert int(h.max()) + 1 <= w.T
