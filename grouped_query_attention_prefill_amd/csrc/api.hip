@@ -5,8 +5,10 @@
 #include "gqa.h"
 #include "internal.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 namespace {
 
@@ -59,6 +61,40 @@ int run_attention(const AttnArgs& a, int in_dtype, void* stream) {
   return hip_status(e);
 }
 
+}  // namespace
+
+// ---- gqa_decode_noalloc: the decode workspace in a static device array.
+// In host code `scratch` names a host-side stand-in, not device memory: its device
+// address is taken once per device with hipGetSymbolAddress (with that device
+// current) and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[GQA_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up on the first call
+// made on each device.
+hipError_t current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 }  // namespace
 
 extern "C" {
@@ -229,7 +265,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
                        float scale, int in_dtype, int out_dtype,
                        void* workspace, size_t workspace_bytes, void* stream, const AppendIn* ap,
-                       float rope_base = 0.f) {
+                       float rope_base = 0.f, bool check_only = false) {
   if (B < 1 || h_q < 1 || h_kv < 1 || T_cap < 1 || d_h < 1) return GQA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (max_seq_len > T_cap) return GQA_ERR_INVALID_ARGUMENT;
@@ -253,6 +289,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   gqa::DecodePlan pl{};
+  if (check_only) return GQA_OK;   // argument checks only (the workspace is the caller's next step)
   if (in_dtype == GQA_BF16) {
     pl = gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, len);
     if (pl.n_split > 1) {
@@ -337,6 +374,25 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, max_seq_len, scale,
                      in_dtype, out_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                       int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+                       float scale, int in_dtype, int out_dtype, void* stream) {
+  // every argument is checked first, then the scratch the split plan needs, all
+  // before the scratch's address is looked up and before any launch
+  const int pre = decode_impl(q, k_cache, v_cache, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, max_seq_len,
+                              scale, in_dtype, out_dtype, nullptr, 0, nullptr, nullptr, 0.f, /*check_only=*/true);
+  if (pre != GQA_OK) return pre;
+  if (in_dtype == GQA_BF16) {
+    const gqa::DecodePlan pl = gqa::plan_decode_bf16(B, h_q, h_kv, T_cap, d_h, max_seq_len > 0 ? max_seq_len : T_cap);
+    if (pl.n_split > 1 && pl.workspace_bytes > GQA_DECODE_SCRATCH_BYTES) return GQA_ERR_SCRATCH_LIMIT;
+  }
+  void* ws = nullptr;
+  if (current_scratch(&ws) != hipSuccess) return GQA_ERR_HIP;
+  return decode_impl(q, k_cache, v_cache, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, max_seq_len, scale,
+                     in_dtype, out_dtype, ws, GQA_DECODE_SCRATCH_BYTES, stream, nullptr);
 }
 
 int gqa_append_decode(const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
@@ -495,6 +551,9 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: unsupported dtype / head-width combination";
     case GQA_ERR_WORKSPACE_TOO_SMALL: return "GQA_ERR_WORKSPACE_TOO_SMALL: decode workspace below gqa_decode_workspace_bytes()";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: HIP launch failure";
+    case GQA_ERR_SCRATCH_LIMIT:
+      return "GQA_ERR_SCRATCH_LIMIT: these sizes need more decode scratch than the library's static "
+             "buffer (GQA_DECODE_SCRATCH_BYTES, 16 MiB); use gqa_decode with a workspace";
     default: return "unknown gqa status";
   }
 }

@@ -22,6 +22,8 @@ GQA_ERR_INVALID_ARGUMENT = 1
 GQA_ERR_UNSUPPORTED = 2
 GQA_ERR_WORKSPACE_TOO_SMALL = 3
 GQA_ERR_HIP = 4
+GQA_ERR_SCRATCH_LIMIT = 5
+GQA_DECODE_SCRATCH_BYTES = 16 << 20
 GQA_F32 = 0
 GQA_BF16 = 1
 GQA_MASK_NONE = 0
@@ -57,6 +59,7 @@ SIGNATURES = {
     "gqa_prefill_backward_workspace_bytes": (_S, [_I, _I, _I]),
     "gqa_prefill_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I, _I,
                                   _P, _S, _P]),
+    "gqa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "gqa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -292,6 +295,38 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, *, q_pos=None, scale: Optional[flo
     _launch(q.device, (("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("workspace", workspace)),
             lib.gqa_decode, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(q_pos), _ptr(out),
             B, h_q, h_kv, T_cap, d_h, msl, sc, code, oc, _ptr(workspace), ws_have)
+    return out
+
+
+def gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, *, q_pos=None, scale: Optional[float] = None,
+                       max_seq_len: Optional[int] = None, out=None, out_dtype=None):
+    """gqa_decode whose partial states live in the library's static device scratch
+    (GQA_DECODE_SCRATCH_BYTES per GPU): the C call allocates nothing.  Pass ``out``
+    to keep this wrapper from allocating the output.  Calls that overlap on one GPU
+    share that scratch and race."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, n, 4)
+    B, h_q, S_q, d_h = q.shape
+    _require(S_q == 1, "decode takes one query per sequence (S_q = 1)")
+    _require(k_cache.shape == v_cache.shape and k_cache.shape[0] == B and k_cache.shape[3] == d_h,
+             "caches must be (B, h_kv, T_cap, d_h)")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q and caches must share a dtype")
+    h_kv, T_cap = k_cache.shape[1], k_cache.shape[2]
+    code = _dtype_code(q)
+    oc = _out_code(code, out_dtype if out is None else out.dtype)
+    if out is None:
+        out = torch.empty((B, h_q, 1, d_h), dtype=_torch_dtype(oc), device=q.device)
+    _dev_tensor(out, "out", 4)
+    _require(tuple(out.shape) == (B, h_q, 1, d_h), "out must be (B, h_q, 1, d_h)")
+    seq_lens = _int_vec(seq_lens, "seq_lens", B, q.device)
+    _require(seq_lens is not None, "seq_lens is required")
+    q_pos = _int_vec(q_pos, "q_pos", B, q.device)
+    sc = 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+    msl = 0 if max_seq_len is None else int(max_seq_len)
+    _launch(q.device, (("k_cache", k_cache), ("v_cache", v_cache), ("out", out)), load_library().gqa_decode_noalloc,
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(q_pos), _ptr(out),
+            B, h_q, h_kv, T_cap, d_h, msl, sc, code, oc)
     return out
 
 

@@ -69,8 +69,12 @@ typedef enum {
   GQA_ERR_INVALID_ARGUMENT = 1,
   GQA_ERR_UNSUPPORTED = 2,
   GQA_ERR_WORKSPACE_TOO_SMALL = 3,
-  GQA_ERR_HIP = 4
+  GQA_ERR_HIP = 4,
+  GQA_ERR_SCRATCH_LIMIT = 5
 } gqa_status_t;
+
+/* Size of the library's static device scratch used by gqa_decode_noalloc (per GPU). */
+#define GQA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
 
 typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype_t;
 
@@ -377,6 +381,29 @@ int gqa_rope_qk(const void* q, void* q_out, const void* k, void* k_out, const in
 int gqa_kv_append_rope(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                        const int32_t* write_pos, int B, int h_kv, int T_cap, int d_h, float base,
                        int dtype, void* stream);
+
+/*
+ * gqa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that forbid allocation, harnesses without an
+ * allocator): the same call, results bit-identical to gqa_decode with a large
+ * enough workspace, but the partial softmax states live in a static device
+ * array inside the library, GQA_DECODE_SCRATCH_BYTES (16 MiB) per GPU, held
+ * from the first call on that GPU until the process ends.  Nothing is
+ * allocated or freed by this call.  The caller still passes q, the caches,
+ * seq_lens, q_pos and o.  Shapes whose split plan needs more than
+ * GQA_DECODE_SCRATCH_BYTES (gqa_decode_workspace_bytes(...) above it) return
+ * GQA_ERR_SCRATCH_LIMIT before anything is launched.  The scratch needs no
+ * clearing: every partial state a call merges is written earlier in that call.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one
+ * GPU (concurrent streams, or threads) race and give undefined results; calls
+ * ordered on one stream are safe.  The first call on each GPU must find that GPU
+ * current (it records the array's address for it).  Arguments and other errors
+ * as gqa_decode.
+ */
+int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int32_t* q_pos, void* o,
+                       int B, int h_q, int h_kv, int T_cap, int d_h, int max_seq_len,
+                       float scale, int in_dtype, int out_dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gqa_status_string(int status);

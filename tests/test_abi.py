@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
               "gqa_rope", "gqa_rope_qk", "gqa_kv_append_rope", "gqa_prefill_lse", "gqa_prefill_backward",
               "gqa_prefill_backward_workspace_bytes", "gqa_append_decode", "gqa_append_decode_paged",
               "gqa_prefill_rope", "gqa_append_decode_rope", "gqa_prefill_chunk_rope", "gqa_kv_append_paged_rope",
-              "gqa_append_decode_paged_rope"):
+              "gqa_append_decode_paged_rope", "gqa_decode_noalloc"):
         assert n in names
     assert set(names) == set(ops.SIGNATURES), "binding prototypes must match the header"
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert ops.gqa_status_string(s).startswith("GQA_")
     assert "unknown" in ops.gqa_status_string(99)
 
@@ -372,3 +372,30 @@ def test_binding_rejects_other_output_dtypes_before_any_call(monkeypatch):
     assert ops._out_code(ops.GQA_BF16, torch.float32) == ops.GQA_F32
     assert ops._out_code(ops.GQA_BF16, torch.bfloat16) == ops.GQA_BF16
 
+
+@needs_lib
+def test_decode_noalloc_validation_and_scratch_limit():
+    """The allocation-free decode checks its arguments as gqa_decode does, then
+    rejects shapes whose split plan needs more than the static scratch -- all before
+    the scratch's address is looked up or anything is launched (no GPU here)."""
+    lib = ops.load_library()
+    cap = ops.GQA_DECODE_SCRATCH_BYTES
+    # (q, k, v, seq_lens, q_pos, o, B, h_q, h_kv, T_cap, d_h, msl, scale, in, out, stream)
+    # one sequence of 2^23 keys over 16 query heads: 2048 splits of 16 x 130 floats
+    big = (FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 16, 1, 1 << 23, 128, 0, 0.088, ops.GQA_BF16, ops.GQA_F32, None)
+    assert lib.gqa_decode_workspace_bytes(1, 16, 1, 1 << 23, 128, ops.GQA_BF16) > cap
+    assert lib.gqa_decode_noalloc(*big) == ops.GQA_ERR_SCRATCH_LIMIT
+    assert "16 MiB" in ops.gqa_status_string(ops.GQA_ERR_SCRATCH_LIMIT)
+    # argument errors come first, whatever the size
+    bad = list(big); bad[3] = None
+    assert lib.gqa_decode_noalloc(*bad) == ops.GQA_ERR_INVALID_ARGUMENT
+    bad = list(big); bad[11] = (1 << 23) + 1              # max_seq_len above capacity
+    assert lib.gqa_decode_noalloc(*bad) == ops.GQA_ERR_INVALID_ARGUMENT
+    bad = list(big); bad[8] = 3                           # 16 % 3 != 0
+    assert lib.gqa_decode_noalloc(*bad) == ops.GQA_ERR_INVALID_ARGUMENT
+    bad = list(big); bad[10] = 96                         # bf16 d_h 96
+    assert lib.gqa_decode_noalloc(*bad) == ops.GQA_ERR_UNSUPPORTED
+    # every benchmarked decode shape fits the scratch
+    for (B, hq, hkv, T) in ((64, 32, 8, 8192), (8, 32, 32, 32000), (8, 32, 8, 32000), (8, 32, 1, 32000),
+                            (32, 64, 8, 32832)):
+        assert lib.gqa_decode_workspace_bytes(B, hq, hkv, T, 128, ops.GQA_BF16) <= cap
