@@ -3,8 +3,8 @@
 //
 // Method ([EffSeq] 分块注意力 and 在线 softmax; [AttnVar] 3.5): the score and
 // probability matrices are never written to memory.  A workgroup owns 256
-// query rows of one (sequence b, K/V head g) and walks the keys in 64-key
-// tiles.  Each K tile and V tile is loaded from HBM once per workgroup into
+// query rows of one (sequence b, K/V head g) and walks the keys in 128-key
+// tiles.  Each K tile and V tile is loaded from memory once per workgroup into
 // LDS and serves every query head of the group that the workgroup holds
 // ([MhaMqaGqa] section 7: one K/V tile serves all r query rows of its group;
 // rows are positions x heads and keep their own causal position); its 8 waves
@@ -22,25 +22,23 @@
 //
 // Schedule: the work of a tile is split into a matrix phase (O^T += V^T P^T for
 // the previous tile, then S^T = K Q^T for this one) and a vector phase (mask,
-// maximum, exponentials, row sums, P packed to bf16).  The 8 waves form two
-// groups of four, one wave of each on every SIMD, and the second group runs one
-// phase behind the first: while one wave of a SIMD keeps the matrix core busy,
-// the other does its exponentials, and a workgroup barrier between phases keeps
-// the two groups in step.  The groups also split the staging: the leading group
-// streams K tiles and the trailing group V tiles, each through registers into
-// a double-buffered LDS stage, written in the middle of the group's matrix phase
-// (global loads are requested two phases before their data is written).  A
-// matrix phase opens with a few QK products whose K operands were read before
-// its barrier.  The ROPE instances rotate the workgroup's Q rows at their
-// positions (in LDS, once the first tile's loads are issued) before the loop.
-// O is written through LDS as whole 128-byte lines with the non-temporal hint.
+// maximum, exponentials, row sums, P packed to bf16 in the score registers).  The
+// 8 waves form two groups of four, one wave of each on every SIMD, and the second
+// group runs one phase behind the first: while one wave of a SIMD keeps the matrix
+// core busy, the other does its exponentials, and a workgroup barrier between
+// phases keeps the two groups in step.  The leading group stages the tiles: early
+// in its matrix phase t it requests K tile t + 1 and V tile t with buffer loads
+// that write LDS directly (no registers pass them), and it waits for them at the
+// end of its next vector phase, two phases later.  The ROPE instances rotate the
+// workgroup's Q rows at their positions (in LDS, before any tile is loaded).  O is
+// written through LDS as whole 128-byte lines with the non-temporal hint.
 //
-// Layouts in LDS, both filled by 16-byte buffer loads that return zeros past the
-// last visible key (no per-load branches):
-//   K [64 keys][d_h] row-major, rows padded by 16 bytes: 16-byte operand reads
+// Layouts in LDS, filled 1 KiB per load instruction (64 lanes x 16 bytes); keys
+// past the last visible one read as zeros (the buffer range ends there):
+//   K [128 keys][d_h] row-major, rows padded by 16 bytes: 16-byte operand reads
 //     are conflict-free at this stride (at 32 bytes of padding they take twice
 //     the cycles)
-//   V [64 keys][d_h] row-major, rows padded by 32 bytes, read with transposing
+//   V [128 keys][d_h] row-major, rows padded by 32 bytes, read with transposing
 //     reads that hand the PV product its V^T operand directly (those cost the
 //     same at every stride and layout measured).
 #include <type_traits>
@@ -55,7 +53,7 @@ namespace {
 constexpr int kThreads = 512;   // 8 waves: two groups of 4, one wave of each per SIMD
 constexpr int kGroup = 256;     // threads per group
 constexpr int kRowsWG = 256;    // query rows per workgroup (32 per wave)
-constexpr int kTile = 64;       // keys per tile
+constexpr int kTile = 128;      // keys per tile
 
 struct PrefillParams {
   const uint16_t* q;
@@ -76,6 +74,10 @@ struct PrefillParams {
   RopeTheta rope_theta;
 };
 
+// LDS: two K stages, then two V stages, each a 128-key tile with padded rows.  The
+// stages are filled by buffer loads that write LDS directly, 1 KiB per instruction
+// (64 lanes x 16 bytes, lane i at byte 16 i); a lane whose 16 bytes fall in a row's
+// padding is switched off, so the padding is never written.
 template <int D>
 struct PrefillLds {
   static constexpr int KS = D * 2 + 16;          // K row stride, bytes
@@ -84,6 +86,76 @@ struct PrefillLds {
   static constexpr int V_STAGE = kTile * VS;
   static constexpr int V_OFF = 2 * K_STAGE;      // two K stages, then two V stages
   static constexpr int TOTAL = 2 * K_STAGE + 2 * V_STAGE;
+  static constexpr int K_BLOCKS = K_STAGE / 1024;
+  static constexpr int V_BLOCKS = V_STAGE / 1024;
+  static constexpr int MAXB = (V_BLOCKS + 3) / 4; // 1 KiB blocks per wave and tile (four waves per group)
+  static_assert(K_STAGE % 1024 == 0 && V_STAGE % 1024 == 0, "stages are whole 1 KiB blocks");
+  static_assert(V_BLOCKS >= K_BLOCKS, "the V stage is the larger");
+  static_assert(TOTAL <= 160 * 1024, "fits the LDS of one CU");
+};
+
+// One 16-byte-per-lane buffer load written straight into LDS: lane i's 16 bytes from
+// byte voff + soff of the descriptor's range land at dst + 16 i (dst wave-uniform).
+// A plain device function, so that only the device compilation sees the LDS pointer.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): the buffer loads that write LDS are counted only by vmcnt; the
+// loading waves wait for them explicitly, at the end of the phase before the one that
+// reads the stage, and the next stage_barrier hands the stage to the other waves.
+__device__ __forceinline__ void wait_lds_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier between phases: this wave's LDS reads and writes are complete
+// (lgkmcnt(0)); no memory access is moved across it by the compiler (the empty asm
+// statements clobber memory) and no instruction by its scheduler (sched_barrier), so
+// each phase's work stays on its side.  Unlike a release fence, it does not wait for
+// the tile loads still in flight into LDS, which are waited for by wait_lds_loads.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Products of one matrix phase in issue order.  QK product (kb, kd): S^T block kb (32
+// keys) += K-chunk x Q-chunk kd (16 values of d); PV product (kc, db): O^T block db (32
+// values of d) += V^T x P^T over 16-key chunk kc.  P^T of chunk kc lives in the first
+// half of the score registers of block kc / 2, so the PV products of chunks 2 kb and
+// 2 kb + 1 come before the QK product that overwrites block kb; consecutive products
+// never write the same accumulator.
+template <int D, bool QK, bool PV>
+struct PhaseOrder {
+  static constexpr int NKD = D / 16;             // QK products per key block
+  static constexpr int NDB = D / 32;             // PV products per key chunk
+  static constexpr int SEG = 2 * NDB;            // == NKD
+  static constexpr int N = (QK ? 4 * NKD : 0) + (PV ? 8 * NDB : 0);
+  // returns pv * 256 + x * 16 + y with (x, y) = (kc, db) or (kb, kd)
+  static constexpr int at(int j) {
+    if (QK && PV) {
+      if (j < SEG) return 256 + (j / NDB) * 16 + j % NDB;
+      if (j < 3 * SEG) {
+        const int m = j - SEG;
+        return (m & 1) ? 256 + (2 + (m / 2) / NDB) * 16 + (m / 2) % NDB : 0 * 16 + m / 2;
+      }
+      if (j < 5 * SEG) {
+        const int m = j - 3 * SEG;
+        return (m & 1) ? 256 + (4 + (m / 2) / NDB) * 16 + (m / 2) % NDB : 1 * 16 + m / 2;
+      }
+      if (j < 6 * SEG) return 256 + (6 + (j - 5 * SEG) / NDB) * 16 + (j - 5 * SEG) % NDB;
+      const int m = j - 6 * SEG;
+      return (2 + (m & 1)) * 16 + m / 2;
+    }
+    if (QK) return (2 * (j / (2 * NKD)) + (j & 1)) * 16 + (j % (2 * NKD)) / 2;
+    return 256 + (j / NDB) * 16 + j % NDB;
+  }
 };
 
 template <int D, bool OUT_BF16, bool ROPE>
@@ -95,8 +167,8 @@ prefill_bf16_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;     // 0: leads, streams K; 1: one phase behind, streams V
-  const int gtid = tid & (kGroup - 1);
+  const int grp = wave >> 2;     // 0: leads, stages K; 1: one phase behind, stages V
+  const int gw = wave & 3;       // wave within the group
   const int h = lane >> 5;       // lane half
   const int col = lane & 31;     // query row within the wave
 
@@ -141,10 +213,9 @@ prefill_bf16_kernel(PrefillParams p) {
     }
   }
   // Rotary encoding at each row's absolute position, applied to the workgroup's Q
-  // rows staged in LDS (free until the first tile is stored): wave w turns the pairs
-  // 8 w .. 8 w + 7 of rows lane + 64 k, so its angles are wave-uniform; then every
-  // lane reads its fragments as above.  Called once the first tile's loads are in
-  // flight, so their latency covers this work.
+  // rows staged in LDS before any tile is loaded: wave w turns the pairs 8 w .. 8 w + 7
+  // of rows lane + 64 k, so its angles are wave-uniform; then every lane reads its
+  // fragments as above.
   auto load_q_rotated = [&]() {
     constexpr int QS = D * 2 + 16;                       // row stride, bytes (<= the K/V stages)
     constexpr int CH = D / 8;                            // 16-byte chunks per row
@@ -194,129 +265,110 @@ prefill_bf16_kernel(PrefillParams p) {
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY;   // unscaled running maximum of this row
   float l_run = 0.f;         // this lane's share of the normalizer
-  f32x16 sacc[2];            // S^T of the current tile, two 32-key halves
-  bf16x8 pf[4];              // P^T of the previous tile, four 16-key chunks
+  // S^T of the current tile, four 32-key blocks.  After the vector phase the first
+  // eight values of block kb hold P^T of chunks 2 kb and 2 kb + 1 as packed bf16.
+  f32x16 sacc[4];
 
-  // ---- staging: this group's tensor (K or V), global -> registers -> LDS
+  // ---- staging: K and V tiles straight from memory into their stages, all requested
+  // by the leading group.  Tile t of the (b, g) slice goes to stage t & 1; 1 KiB block j
+  // of a stage is written by leading wave j % 4.  *_off[i] is this lane's byte offset
+  // within a tile for block gw + 4 i.  Keys at or past kv_end read as zeros (the
+  // descriptors' range ends there); a lane whose 16 bytes are row padding reads at
+  // 2^31, past any range the API admits (a head's slice is below 2^31 bytes), so it
+  // touches no memory and writes zeros into padding no product reads.
   const size_t kv_base = (size_t)(b * p.h_kv + g) * p.T_cap * D;
-  const uint32_t slice_bytes = (uint32_t)kv_end * D * 2;     // keys >= kv_end read as zeros
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc((grp == 0 ? p.k : p.v) + kv_base, slice_bytes);
-  const int s_stride = grp == 0 ? L::KS : L::VS;
-  unsigned char* const s_base = lds + (grp == 0 ? 0 : L::V_OFF);
-  const int s_stage = grp == 0 ? L::K_STAGE : L::V_STAGE;
-  constexpr int UNITS = kTile * D / 8 / kGroup;             // 16-byte chunks per thread
-  uint4 sreg[UNITS];
-  auto load_tile = [&](int t) {
+  const uint32_t slice_bytes = (uint32_t)kv_end * D * 2;
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + kv_base, slice_bytes);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + kv_base, slice_bytes);
+  uint32_t k_off[L::MAXB], v_off[L::MAXB];
 #pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      const int u = gtid + kGroup * i;
-      const int row = u / (D / 8), c8 = u % (D / 8);
-      sreg[i] = load16(srs, (uint32_t)((t * kTile + row) * D + c8 * 8) * 2);
-    }
+  for (int i = 0; i < L::MAXB; ++i) {
+    const int a = (gw + 4 * i) * 1024 + lane * 16;
+    const int rk = a / L::KS, ok = a - rk * L::KS;
+    const int rv = a / L::VS, ov = a - rv * L::VS;
+    k_off[i] = ok < D * 2 ? (uint32_t)(rk * D * 2 + ok) : 0x80000000u;
+    v_off[i] = ov < D * 2 ? (uint32_t)(rv * D * 2 + ov) : 0x80000000u;
+  }
+  // Block i of this wave's share of tile t of K (or V) into `stage`.
+  auto load_k_block = [&](unsigned char* stage, const int t, const int i) {
+    if (gw + 4 * i < L::K_BLOCKS)
+      load_lds16(k_rs, stage + (gw + 4 * i) * 1024, k_off[i], (uint32_t)t * kTile * D * 2);
   };
-  auto store_tile = [&](int t) {
-    unsigned char* dst = s_base + (t & 1) * s_stage;
+  auto load_v_block = [&](unsigned char* stage, const int t, const int i) {
+    if (gw + 4 * i < L::V_BLOCKS)
+      load_lds16(v_rs, stage + (gw + 4 * i) * 1024, v_off[i], (uint32_t)t * kTile * D * 2);
+  };
+  auto load_k_tile = [&](unsigned char* stage, const int t) {
 #pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      const int u = gtid + kGroup * i;
-      const int row = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<uint4*>(dst + row * s_stride + c8 * 16) = sreg[i];
-    }
+    for (int i = 0; i < L::MAXB; ++i) load_k_block(stage, t, i);
   };
-
-  // ---- staging duty of matrix phase t.  Leading group: K tile t + 1 to LDS, K tile
-  // t + 2 requested.  Trailing group: V tile t to LDS, V tile t + 1 requested.
-  // Each write goes to the stage whose previous tile both groups have finished.
-  auto stage_duty = [&](const int t) {
-    const int ts = grp == 0 ? t + 1 : t;
-    if (ts < n_tiles) {
-      store_tile(ts);
-      if (ts + 1 < n_tiles) load_tile(ts + 1);
-    }
+  auto load_v_tile = [&](unsigned char* stage, const int t) {
+#pragma unroll
+    for (int i = 0; i < L::MAXB; ++i) load_v_block(stage, t, i);
   };
+  auto k_stage = [&](const int t) { return lds + (t & 1) * L::K_STAGE; };
+  auto v_stage = [&](const int t) { return lds + L::V_OFF + (t & 1) * L::V_STAGE; };
 
   // ---- matrix phase t: O^T += V^T P^T for tile t - 1 (PV) and S^T = K Q^T for tile t
-  // (QK).  Operand reads run kWin ahead of the products that consume them, in an
-  // order pinned by scheduling barriers, alternating QK and PV products so that no
-  // accumulator is needed again before the product writing it has finished.
-  constexpr int NOP = D / 8;     // operands per product kind and tile
+  // (QK), in PhaseOrder.  Operand reads run kWin products ahead of the products that
+  // consume them, in an order pinned by scheduling barriers.  After product kLoadAt the
+  // leading group requests K tile t + 1 (into kdst) and V tile t (into vdst), stages no
+  // wave reads before the barrier that ends the next phase (see the pipeline below), so
+  // the loads have two phases to land.  The four stage pointers are restrict-qualified
+  // because they never overlap; that also tells the compiler that the phase's LDS reads
+  // need not wait for the loads just requested.
   constexpr int kWin = 8;
-  constexpr int kStageAt = 8;    // staging duty is issued after this many products
-  // The first NPRE QK operands of matrix phase t are read at the end of the vector
-  // phase before it, ahead of the barrier, so the phase opens with products whose
-  // operands are already in registers while its V reads are still in flight.  K
-  // tile t was written during the leading group's matrix phase t - 1 and a barrier
-  // has passed since; its stage is next written with K tile t + 2, in matrix phase
-  // t + 1 of the leading group, after both groups' matrix phase t.
-  constexpr int NPRE = 4;
+  constexpr int kLoadAt = 1;
   bf16x8 ops[kWin];
-  auto pre_read = [&](const int t) {
-    const unsigned char* ks_ = lds + (t & 1) * L::K_STAGE;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i)
-      ops[i] = *reinterpret_cast<const bf16x8*>(ks_ + ((i & 1) * 32 + col) * L::KS + ((i >> 1) * 16 + h * 8) * 2);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto matrix_phase = [&](const int t, auto qk_tag, auto pv_tag, auto pre_tag) {
+  auto matrix_phase = [&](const int t, auto qk_tag, auto pv_tag, unsigned char* __restrict__ kdst,
+                          unsigned char* __restrict__ vdst, const unsigned char* __restrict__ ks_,
+                          const unsigned char* __restrict__ vs_) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
-    constexpr bool PRE = decltype(pre_tag)::value;
-    constexpr int N = (QK ? NOP : 0) + (PV ? NOP : 0);
-    const unsigned char* ks_ = lds + (t & 1) * L::K_STAGE;
-    const unsigned char* vs_ = lds + L::V_OFF + ((t - 1) & 1) * L::V_STAGE;
-    // order: NPRE QK products first (their operands were read before the barrier),
-    // then PV and QK alternating, then the remaining PV products
-    auto is_pv = [&](int j) -> bool {
-      if (!(QK && PV)) return PV;
-      if (j < NPRE) return false;
-      const int m = j - NPRE;
-      if (m < 2 * (NOP - NPRE)) return (m & 1) == 0;
-      return true;
-    };
-    auto idx = [&](int j) -> int {
-      if (!(QK && PV)) return j;
-      if (j < NPRE) return j;
-      const int m = j - NPRE;
-      if (m < 2 * (NOP - NPRE)) return (m & 1) == 0 ? m / 2 : NPRE + m / 2;
-      return (NOP - NPRE) + (m - 2 * (NOP - NPRE));
-    };
+    using O = PhaseOrder<D, QK, PV>;
+    constexpr int N = O::N;
     auto read = [&](int j) -> bf16x8 {
-      const int i = idx(j);
-      if (is_pv(j)) return load_vt_operand(vs_, L::VS, i / (D / 32), (i % (D / 32)) * 32, lane);
-      return *reinterpret_cast<const bf16x8*>(ks_ + ((i & 1) * 32 + col) * L::KS + ((i >> 1) * 16 + h * 8) * 2);
+      const int c = O::at(j);
+      const int x = (c >> 4) & 15, y = c & 15;
+      if (c >= 256) return load_vt_operand(vs_, L::VS, x, y * 32, lane);
+      return *reinterpret_cast<const bf16x8*>(ks_ + (x * 32 + col) * L::KS + (y * 16 + h * 8) * 2);
     };
 #pragma unroll
-    for (int j = PRE ? NPRE : 0; j < kWin && j < N; ++j) ops[j] = read(j);
+    for (int j = 0; j < kWin && j < N; ++j) ops[j] = read(j);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       __builtin_amdgcn_sched_barrier(0);
-      const int i = idx(j);
-      if (is_pv(j)) {
-        const int kc = i / (D / 32), db = i % (D / 32);
-        oacc[db] = mfma32(ops[j % kWin], pf[kc], oacc[db]);
+      const int c = O::at(j);
+      const int x = (c >> 4) & 15, y = c & 15;
+      if (c >= 256) {
+        const f32x16& sp = sacc[x >> 1];
+        const int e0 = 4 * (x & 1);
+        typedef float f32x4_ __attribute__((ext_vector_type(4)));
+        const f32x4_ w = {sp[e0], sp[e0 + 1], sp[e0 + 2], sp[e0 + 3]};
+        oacc[y] = mfma32(ops[j % kWin], __builtin_bit_cast(bf16x8, w), oacc[y]);
       } else {
-        const int kb = i & 1, kd = i >> 1;
-        sacc[kb] = mfma32(ops[j % kWin], qf[kd], kd == 0 ? f32x16{} : sacc[kb]);
+        sacc[x] = mfma32(ops[j % kWin], qf[y], y == 0 ? f32x16{} : sacc[x]);
       }
       if (j + kWin < N) ops[j % kWin] = read(j + kWin);
-      if (j == kStageAt - 1) {
+      if (QK && j == kLoadAt) {
         __builtin_amdgcn_sched_barrier(0);
-        stage_duty(t);
+        if (grp == 0) {
+          if (t + 1 < n_tiles) load_k_tile(kdst, t + 1);
+          load_v_tile(vdst, t);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- vector phase t: online-softmax update from S^T of tile t, P^T for the next
-  // matrix phase; then this group's staging duty: tile t + 1 to LDS, tile t + 2 requested
+  // ---- vector phase t: online-softmax update from S^T of tile t; P^T packed in place
   auto vector_phase = [&](const int t) {
     const int k0 = t * kTile;
     // mask only where some key of the tile may be invisible to some row
     const bool need_mask = (p.causal && k0 + kTile - 1 > min_pos) || (k0 + kTile > len_b);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -326,7 +378,7 @@ prefill_bf16_kernel(PrefillParams p) {
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = pair_max(mx);
@@ -344,51 +396,55 @@ prefill_bf16_kernel(PrefillParams p) {
     const float mc = (m_run == -INFINITY ? 0.f : m_run) * p.c;
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pe = fast_exp2(fmaf(sacc[kb][e], p.c, -mc));
         sacc[kb][e] = pe;
         psum += pe;
       }
-    l_run += psum;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const f32x16& sv = sacc[kc >> 1];
-      const int e0 = 8 * (kc & 1);
-      pf[kc] = pack_bf16x8(sv[e0], sv[e0 + 1], sv[e0 + 2], sv[e0 + 3], sv[e0 + 4], sv[e0 + 5], sv[e0 + 6], sv[e0 + 7]);
+      f32x16& sv = sacc[kb];
+      const bf16x8 c0 = pack_bf16x8(sv[0], sv[1], sv[2], sv[3], sv[4], sv[5], sv[6], sv[7]);
+      const bf16x8 c1 = pack_bf16x8(sv[8], sv[9], sv[10], sv[11], sv[12], sv[13], sv[14], sv[15]);
+      typedef float f32x4_ __attribute__((ext_vector_type(4)));
+      const f32x4_ w0 = __builtin_bit_cast(f32x4_, c0), w1 = __builtin_bit_cast(f32x4_, c1);
+      sv[0] = w0[0]; sv[1] = w0[1]; sv[2] = w0[2]; sv[3] = w0[3];
+      sv[4] = w1[0]; sv[5] = w1[1]; sv[6] = w1[2]; sv[7] = w1[3];
     }
+    l_run += psum;
   };
 
-  // ---- pipeline.  Phase k of the leading group runs beside phase k - 1 of the
-  // trailing one; both issue the same number of barriers.  K tile t is read in
-  // matrix phase t, V tile t in matrix phase t + 1; a stage is rewritten only
-  // after both groups are past its last reader.
+  // ---- pipeline.  Slot 2t: leading group matrix phase t, trailing group vector phase
+  // t - 1; slot 2t + 1: leading vector t, trailing matrix t; a workgroup barrier ends
+  // every slot.  Matrix phase t reads K tile t and V tile t - 1.  Early in slot 2t the
+  // leading group requests K tile t + 1, into the stage of K tile t - 1 (last read in
+  // slot 2t - 1), and V tile t, into the stage of V tile t - 2 (last read in slot
+  // 2t - 1); it waits for both at the end of slot 2t + 1, before their first reader.
+  // (Phases without QK products request nothing; their unused destination pointers
+  // only keep the four stages distinct.)
   if (n_tiles > 0) {
     const auto yes = std::integral_constant<bool, true>{};
     const auto no = std::integral_constant<bool, false>{};
-    load_tile(0);
     if constexpr (ROPE) load_q_rotated();
-    if (grp == 0) {
-      store_tile(0);
-      if (n_tiles > 1) load_tile(1);
-    }
-    lds_barrier();
-    if (grp == 1) lds_barrier();   // the trailing group starts one phase late
-    matrix_phase(0, yes, no, no);
-    lds_barrier();
+    if (grp == 0) load_k_tile(k_stage(0), 0);
+    wait_lds_loads();               // K tile 0, and every wave's Q fragments
+    stage_barrier();
+    if (grp == 1) stage_barrier();  // the trailing group starts one phase late
+    matrix_phase(0, yes, no, k_stage(1), v_stage(0), k_stage(0), v_stage(1));
+    stage_barrier();
     vector_phase(0);
-    if (1 < n_tiles) pre_read(1);
-    lds_barrier();
+    if (grp == 0) wait_lds_loads(); // K tile 1, V tile 0
+    stage_barrier();
     for (int t = 1; t < n_tiles; ++t) {
-      matrix_phase(t, yes, yes, yes);
-      lds_barrier();
+      matrix_phase(t, yes, yes, k_stage(t + 1), v_stage(t), k_stage(t), v_stage(t - 1));
+      stage_barrier();
       vector_phase(t);
-      if (t + 1 < n_tiles) pre_read(t + 1);
-      lds_barrier();
+      if (grp == 0) wait_lds_loads();   // K tile t + 1, V tile t
+      stage_barrier();
     }
-    matrix_phase(n_tiles, no, yes, no);
-    if (grp == 0) lds_barrier();   // pairs with the trailing group's last barrier
+    matrix_phase(n_tiles, no, yes, k_stage(n_tiles + 1), v_stage(n_tiles), k_stage(n_tiles),
+                 v_stage(n_tiles - 1));
+    if (grp == 0) stage_barrier();  // pairs with the trailing group's last barrier
   }
 
   // ---- epilogue: o = u / l
