@@ -429,6 +429,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy", "rope", "backward"],
                     help="run one part alone (for profiler runs); prints that part's JSON")
+    ap.add_argument("--workload", action="append", default=None,
+                    help="with --only sweep: run only this sweep entry (NAME, or NAME:PAGE for a paged cache); "
+                         "may be repeated")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -461,6 +464,12 @@ def main():
     if args.only in ("decode", "sweep"):
         flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         runs = [("decode_bf16_B64_T8192", 0)] if args.only == "decode" else SWEEP
+        if args.only == "sweep" and args.workload:
+            want = [(w.split(":")[0], int(w.split(":")[1]) if ":" in w else 0) for w in args.workload]
+            unknown = [w for w in want if w not in SWEEP]
+            if unknown:
+                raise SystemExit(f"unknown sweep entries {unknown}; choose from {SWEEP}")
+            runs = want
         print(json.dumps([bench_decode(n, steps, warmup, flush_buf, ps)[0] for n, ps in runs]), flush=True)
         return
 

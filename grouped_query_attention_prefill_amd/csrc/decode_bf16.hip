@@ -93,6 +93,66 @@ __device__ __forceinline__ uint4 new_key_chunk(const DecodeParams& p, int b, int
   return x;
 }
 
+// The end of a workgroup: its 4 waves' states of HN query heads, held in LDS as
+// mo [wave][head][D + 4] (unnormalized outputs; rows padded so that the float4
+// reads below meet distinct banks) and mml [wave][head][2] (m * c, l), are merged
+// with the rule of [AttnVar] 3.5 and stored: the normalized output when the slice
+// is the whole history, else the partial state (m, l, u) for the combine kernel.
+// Each half-wave takes one head and covers its D values in float4 units, so every
+// store writes whole rows of contiguous memory.
+template <int D>
+constexpr int merge_stride() { return D + 4; }
+template <int D, int HN>
+constexpr int merge_bytes() { return 4 * HN * merge_stride<D>() * 4 + 4 * HN * 2 * 4; }
+
+template <int D, int HN, bool OUT_BF16>
+__device__ __forceinline__ void merge_and_store(const DecodeParams& p, const float* mo, const float* mml, int b,
+                                                int head0, int n_heads, int split, int tid) {
+  constexpr int MS = merge_stride<D>();
+  static_assert(D / 4 <= 32, "one half-wave covers a head's row");
+  const int dq = tid & 31;                  // float4 unit of the row (D / 4 of them)
+  if (dq >= D / 4) return;
+#pragma unroll
+  for (int rnd = 0; rnd < HN / 8; ++rnd) {
+    const int j = rnd * 8 + (tid >> 5);     // head of the workgroup
+    if (j >= n_heads) continue;
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { mw[w] = mml[(w * HN + j) * 2]; M = fmaxf(M, mw[w]); }
+    float wgt[4], lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wgt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
+      lsum += wgt[w] * mml[(w * HN + j) * 2 + 1];
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 u = *reinterpret_cast<const float4*>(mo + (w * HN + j) * MS + 4 * dq);
+      acc.x += wgt[w] * u.x; acc.y += wgt[w] * u.y; acc.z += wgt[w] * u.z; acc.w += wgt[w] * u.w;
+    }
+    const int head = head0 + j;
+    if (p.direct) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const size_t oi = (size_t)(b * p.h_q + head) * D + 4 * dq;
+      if constexpr (OUT_BF16) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 w4;
+        w4[0] = (__bf16)(acc.x * inv); w4[1] = (__bf16)(acc.y * inv);
+        w4[2] = (__bf16)(acc.z * inv); w4[3] = (__bf16)(acc.w * inv);
+        *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + oi) = w4;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.o) + oi) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      }
+    } else {
+      const size_t pidx = (size_t)(b * p.h_q + head) * p.n_split_cap + split;
+      *reinterpret_cast<float4*>(p.ws_u + pidx * D + 4 * dq) = acc;
+      if (dq == 0) *reinterpret_cast<float2*>(p.ws_ml + pidx * 2) = make_float2(M, lsum);
+    }
+  }
+}
+
 template <int D>
 struct DecodeLds {
   static constexpr int KS = D * 2 + 16;
@@ -100,7 +160,7 @@ struct DecodeLds {
   static constexpr int K_BYTES = kTile * KS;
   static constexpr int STAGE = K_BYTES + kTile * VS;
   // the end-of-slice merge reuses the stage: 4 waves x 32 rows x D floats + (m, l)
-  static constexpr int MERGE = 4 * 32 * D * 4 + 4 * 32 * 2 * 4;
+  static constexpr int MERGE = merge_bytes<D, 32>();
   static constexpr int TOTAL = STAGE > MERGE ? STAGE : MERGE;
 };
 
@@ -334,68 +394,24 @@ decode_bf16_kernel(DecodeParams p) {
 
   // ---- merge the 4 waves' states in LDS
   lds_barrier();
-  float* mo = reinterpret_cast<float*>(lds);              // [wave][D][32]
-  float* mml = mo + 4 * D * 32;                            // [wave][32][2]
+  constexpr int MS = merge_stride<D>();
+  float* mo = reinterpret_cast<float*>(lds);              // [wave][32][MS]
+  float* mml = mo + 4 * 32 * MS;                           // [wave][32][2]
   const float l_pair = pair_sum(l_run);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int d = db * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-      mo[(wave * D + d) * 32 + col] = oacc[db][e];
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int d = db * 32 + 8 * e4 + 4 * h;
+      *reinterpret_cast<float4*>(mo + (wave * 32 + col) * MS + d) =
+          make_float4(oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]);
     }
   if (h == 0) {
     mml[(wave * 32 + col) * 2 + 0] = (m_run == -INFINITY) ? -INFINITY : m_run * p.c;
     mml[(wave * 32 + col) * 2 + 1] = l_pair;
   }
   lds_barrier();
-
-  // thread -> (row j, d range): 32 rows x D values, D / 8 per thread
-  const int j = tid & 31;
-  const int dgrp = tid >> 5;             // 0..7
-  float mw[4], M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) { mw[w] = mml[(w * 32 + j) * 2]; M = fmaxf(M, mw[w]); }
-  float wgt[4], lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    wgt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
-    lsum += wgt[w] * mml[(w * 32 + j) * 2 + 1];
-  }
-  if (j < n_heads_here) {
-    const int head = g * p.r + hcix * 32 + j;
-    if (p.direct) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const int d = dgrp * (D / 8) + i;
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc += wgt[w] * mo[(w * D + d) * 32 + j];
-        const size_t oi = (size_t)(b * p.h_q + head) * D + d;
-        if constexpr (OUT_BF16) {
-          __bf16 x = (__bf16)(acc * inv);
-          static_cast<uint16_t*>(p.o)[oi] = __builtin_bit_cast(uint16_t, x);
-        } else {
-          static_cast<float*>(p.o)[oi] = acc * inv;
-        }
-      }
-    } else {
-      const size_t pidx = (size_t)(b * p.h_q + head) * p.n_split_cap + split;
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const int d = dgrp * (D / 8) + i;
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc += wgt[w] * mo[(w * D + d) * 32 + j];
-        p.ws_u[pidx * D + d] = acc;
-      }
-      if (dgrp == 0) {
-        p.ws_ml[pidx * 2 + 0] = M;
-        p.ws_ml[pidx * 2 + 1] = lsum;
-      }
-    }
-  }
+  merge_and_store<D, 32, OUT_BF16>(p, mo, mml, b, g * p.r + hcix * 32, n_heads_here, split, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -431,7 +447,7 @@ struct Decode16Lds {
   static constexpr int VS = D * 2 + 32;
   static constexpr int K_BYTES = kTile16 * KS;
   static constexpr int STAGE = K_BYTES + kTile16 * VS;
-  static constexpr int MERGE = 4 * 16 * D * 4 + 4 * 16 * 2 * 4;
+  static constexpr int MERGE = merge_bytes<D, 16>();
   static constexpr int TOTAL = STAGE > MERGE ? STAGE : MERGE;
 };
 
@@ -637,58 +653,20 @@ decode16_bf16_kernel(DecodeParams p) {
 
   // ---- merge the 4 waves' states in LDS
   lds_barrier();
-  float* mo = reinterpret_cast<float*>(lds);              // [wave][D][16]
-  float* mml = mo + 4 * D * 16;                            // [wave][16][2]
+  constexpr int MS = merge_stride<D>();
+  float* mo = reinterpret_cast<float*>(lds);              // [wave][16][MS]
+  float* mml = mo + 4 * 16 * MS;                           // [wave][16][2]
   const float l_all = quad_sum(l_run);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mo[(wave * D + dt * 16 + 4 * G + i) * 16 + q16] = oacc[dt][i];
+    *reinterpret_cast<float4*>(mo + (wave * 16 + q16) * MS + dt * 16 + 4 * G) =
+        make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
   if (G == 0) {
     mml[(wave * 16 + q16) * 2 + 0] = (m_run == -INFINITY) ? -INFINITY : m_run * p.c;
     mml[(wave * 16 + q16) * 2 + 1] = l_all;
   }
   lds_barrier();
-
-  // thread -> (head j, d range): 16 heads x D values, D / 16 per thread
-  const int j = tid & 15;
-  const int dgrp = tid >> 4;             // 0..15
-  float mw[4], M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) { mw[w] = mml[(w * 16 + j) * 2]; M = fmaxf(M, mw[w]); }
-  float wgt[4], lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    wgt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
-    lsum += wgt[w] * mml[(w * 16 + j) * 2 + 1];
-  }
-  if (j < n_heads_here) {
-    const int head = g * p.r + j;
-    const size_t pidx = (size_t)(b * p.h_q + head) * p.n_split_cap + split;
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      const int d = dgrp * (D / 16) + i;
-      float acc = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc += wgt[w] * mo[(w * D + d) * 16 + j];
-      if (p.direct) {
-        const size_t oi = (size_t)(b * p.h_q + head) * D + d;
-        if constexpr (OUT_BF16) {
-          __bf16 x = (__bf16)(acc * inv);
-          static_cast<uint16_t*>(p.o)[oi] = __builtin_bit_cast(uint16_t, x);
-        } else {
-          static_cast<float*>(p.o)[oi] = acc * inv;
-        }
-      } else {
-        p.ws_u[pidx * D + d] = acc;
-      }
-    }
-    if (!p.direct && dgrp == 0) {
-      p.ws_ml[pidx * 2 + 0] = M;
-      p.ws_ml[pidx * 2 + 1] = lsum;
-    }
-  }
+  merge_and_store<D, 16, OUT_BF16>(p, mo, mml, b, g * p.r, n_heads_here, split, tid);
 }
 
 // Merge the partial states of one (sequence, query head): [AttnVar] 3.5 applied
