@@ -42,36 +42,165 @@ SETTLE_S = 0.3
 SWEEP = [("decode_mha_B8_T32000", 0), ("decode_gqa_B8_T32000", 0), ("decode_mqa_B8_T32000", 0),
          ("ragged_append_decode_B32", 0), ("ragged_append_decode_B32", 64)]
 
-KERNEL_SOURCES = {
-    "prefill_bf16_kernel": ["prefill_bf16.hip", "mfma_common.h"],
-    "decode_bf16_kernel": ["decode_bf16.hip", "mfma_common.h"],
+# HBM traffic of each timed row's kernel(s), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# (profiles/traffic.json, written by --write-traffic): row -> (bench.py arguments that run
+# it alone, the kernels counted and how, the sources those kernels are built from).  A
+# row's entry counts only while the hash of its sources matches.
+_COMMON = ["internal.h", "mfma_common.h"]
+TRAFFIC_ROWS = {
+    "prefill_causal_bf16_T4096": (["--only", "prefill"], ("prefill_bf16_kernel<128, false, false>", "mean"),
+                                  ["prefill_bf16.hip", "rope_common.h", *_COMMON]),
+    "decode_bf16_B64_T8192": (["--only", "decode"], ("decode_main", "mean"),
+                              ["decode_bf16.hip", "rope_common.h", *_COMMON]),
+    **{(n + (f"_paged{ps}" if ps else "")): (["--only", "sweep", "--workload", n + (f":{ps}" if ps else "")],
+                                             ("decode_main", "mean"), ["decode_bf16.hip", "rope_common.h", *_COMMON])
+       for n, ps in SWEEP},
+    "prefill_causal_bf16_T4096_qk_rope": (["--only", "rope"], ("rope_kernel", "largest_grid"),
+                                          ["rope.hip", "rope_common.h", "internal.h"]),
+    "prefill_causal_bf16_T4096_backward": (["--only", "backward"],
+                                           (("bwd_delta", "bwd_dkdv_kernel", "bwd_dq_kernel"), "sum_of_means"),
+                                           ["backward_bf16.hip", *_COMMON]),
 }
+COPY_ROW = (["--only", "copy"], ("copyBuffer", "mean"))
+TRAFFIC_COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(kernel: str) -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    for f in files:
         with open(os.path.join(ROOT, "grouped_query_attention_prefill_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches the current source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def measured_traffic(row: str):
+    """HBM bytes per launch of the row's kernel(s) from profiles/traffic.json, if the
+    entry was taken from the current sources; else None."""
     try:
-        with open(path) as f:
-            t = json.load(f)
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            e = json.load(f).get("rows", {}).get(row)
     except (OSError, ValueError):
         return None
-    e = t.get(kernel, {}).get(workload)
-    if not e or e.get("source_hash") != source_hash(kernel):
+    if not e or e.get("source_hash") != source_hash(TRAFFIC_ROWS[row][2]):
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+def traffic_commands(out_dir: str):
+    """The rocprofv3 runs behind profiles/traffic.json: one counter per run (FETCH_SIZE
+    alone fills three of the four TCC counters), each bench.py row alone."""
+    runs = [("copy", COPY_ROW[0])] + [(row, spec[0]) for row, spec in TRAFFIC_ROWS.items()]
+    cmds = []
+    for counter in TRAFFIC_COUNTERS:
+        for row, args in runs:
+            d = os.path.join(out_dir, f"{counter.lower()}_{row}")
+            cmds.append((counter, row, d, ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", d,
+                                           "-o", "p", "--", "python3", os.path.join(ROOT, "bench.py"), *args,
+                                           "--steps", "3", "--warmup", "1", "--settle", "0"]))
+    return cmds
+
+
+def _per_dispatch(csv_dir: str, counter: str):
+    """{kernel name: [(grid size, value per dispatch), ...]} from one rocprofv3 --pmc run."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {csv_dir}")
+    per = {}
+    for path in files:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    per.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return per
+
+
+def _select(per, how):
+    """KiB per launch of the selected kernel(s) and the names counted."""
+    what, mode = how
+
+    def match(name, key):
+        if key == "decode_main":
+            return "gqa::" in name and "decode" in name and "_kernel" in name and "combine" not in name
+        return key in name
+
+    if mode == "sum_of_means":
+        total, names = 0.0, []
+        for key in what:
+            hits = [n for n in per if match(n, key)]
+            if len(hits) != 1:
+                raise SystemExit(f"expected one kernel matching {key!r}, found {hits}")
+            vals = [v for _, v in per[hits[0]]]
+            total += sum(vals) / len(vals)
+            names.append(hits[0])
+        return total, names
+    hits = [n for n in per if match(n, what)]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {what!r}, found {hits}")
+    rows = per[hits[0]]
+    if mode == "largest_grid":
+        g = max(gs for gs, _ in rows)
+        rows = [(gs, v) for gs, v in rows if gs == g]
+    vals = [v for _, v in rows]
+    return sum(vals) / len(vals), hits
+
+
+def write_traffic(out_dir: str):
+    """profiles/traffic.json and profiles/hbm_traffic_counters.md from the runs of traffic_commands()."""
+    import subprocess
+
+    dirs = {(c, row): d for c, row, d, _ in traffic_commands(out_dir)}
+    fetch_copy, _ = _select(_per_dispatch(dirs[("FETCH_SIZE", "copy")], "FETCH_SIZE"), COPY_ROW[1])
+    write_copy, _ = _select(_per_dispatch(dirs[("WRITE_SIZE", "copy")], "WRITE_SIZE"), COPY_ROW[1])
+    n = 1 << 30   # the copy reads and writes 1 GiB
+    fs, ws = n / (fetch_copy * 1024), n / (write_copy * 1024)
+    try:
+        rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                             text=True).stdout.strip()
+    except OSError:
+        rev = ""
+    out = {"_calibration": {"copy_bytes_read": n, "copy_bytes_written": n, "copy_FETCH_SIZE_KiB": fetch_copy,
+                            "copy_WRITE_SIZE_KiB": write_copy, "fetch_scale": fs, "write_scale": ws},
+           "source_revision": rev, "rows": {}}
+    table = []
+    for row, (args, how, files) in TRAFFIC_ROWS.items():
+        fk, names = _select(_per_dispatch(dirs[("FETCH_SIZE", row)], "FETCH_SIZE"), how)
+        wk, _ = _select(_per_dispatch(dirs[("WRITE_SIZE", row)], "WRITE_SIZE"), how)
+        rd, wr = round(fk * 1024 * fs), round(wk * 1024 * ws)
+        out["rows"][row] = {"kernels": names, "counted": how[1], "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk,
+                            "read": rd, "written": wr, "hbm_bytes_per_launch": rd + wr,
+                            "source_hash": source_hash(files)}
+        table.append((row, names, fk, wk, rd, wr))
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    cmds = traffic_commands("<out>")
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             f"Source revision: `{rev}`.  Written by `python bench.py --write-traffic <out>` from the runs below "
+             "(one counter per run, each bench.py row alone; `<repo>` is the repository root).", "",
+             "```"]
+    for _, _, _, c in cmds:
+        lines.append("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 " +
+                     " ".join(c).replace(ROOT, "<repo>"))
+    lines += ["```", "",
+              f"Calibration: a plain 1 GiB device copy (`bench.py --only copy`) reports FETCH_SIZE = "
+              f"{fetch_copy:.1f} KiB and WRITE_SIZE = {write_copy:.1f} KiB per dispatch, so FETCH_SIZE is scaled "
+              f"by {fs:.4f} and WRITE_SIZE by {ws:.4f}.", "",
+              "| bench row | kernel(s) counted | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes read (scaled) | "
+              "HBM bytes written (scaled) | total per launch |", "|---|---|---|---|---|---|---|"]
+    for row, names, fk, wk, rd, wr in table:
+        short = " + ".join("`" + nm.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0] + "`"
+                           for nm in names)
+        lines.append(f"| {row} | {short} | {fk:.1f} | {wk:.1f} | {rd:,} | {wr:,} | {rd + wr:,} |")
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out["rows"], indent=1))
 
 
 def settle(fn, seconds: float):
@@ -265,7 +394,7 @@ def bench_decode(name, steps, warmup, flush_buf, page_size=0):
         "value": round(gbs, 1), "unit": "GB/s",
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("decode_bf16_kernel", wname)},
+                     "traffic": measured_traffic(wname)},
         "kernels": "decode split (append fused) + combine" if appended else "decode split + combine",
     }
     if page_size:
@@ -306,8 +435,9 @@ def bench_backward(steps, warmup):
     return {"workload": w.name + "_backward", "algorithmic_flops": flops, "ms_per_call": round(ms, 5),
             "value": round(tf, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
-            "kernels": "delta + dK/dV + dQ", "grad_dtype": "fp32"}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(w.name + "_backward")},
+            "kernels": "delta + dK/dV + dQ (traffic: the three kernels' bytes summed)", "grad_dtype": "fp32"}
 
 
 # ---------------------------------------------------------------------------------------- rotary encoding
@@ -343,7 +473,8 @@ def bench_rope(steps, warmup, flush_buf):
             "algorithmic_bytes": nbytes, "ms_per_call": round(ms, 5), **spread(per), "value": round(gbs, 1),
             "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(w.name + "_qk_rope")},
             "kernels": "rope (Q and K, one launch)",
             "prefill_rope_fused": {"ms_per_call": round(fused_ms, 5),
                                    "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
@@ -429,10 +560,21 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "sweep", "copy", "rope", "backward"],
                     help="run one part alone (for profiler runs); prints that part's JSON")
+    ap.add_argument("--traffic-commands", metavar="OUT",
+                    help="print the rocprofv3 counter runs behind profiles/traffic.json (output under OUT), one a line")
+    ap.add_argument("--write-traffic", metavar="OUT",
+                    help="write profiles/traffic.json and hbm_traffic_counters.md from those runs' output under OUT")
     ap.add_argument("--workload", action="append", default=None,
                     help="with --only sweep: run only this sweep entry (NAME, or NAME:PAGE for a paged cache); "
                          "may be repeated")
     args = ap.parse_args()
+    if args.traffic_commands:
+        for _, _, _, c in traffic_commands(args.traffic_commands):
+            print(" ".join(c))
+        return
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -505,7 +647,7 @@ def main():
                    "causal": True, "out_dtype": "fp32", "algorithmic_flops": pre["flops"]},
         "roofline": {"bound": "mfma", "achieved": round(pre["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre["achieved"] / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_bf16_kernel", w.name),
+                     "traffic": measured_traffic(w.name),
                      "kernel_ms": round(pre["kernel_ms"], 5)},
         "decode": dec,
         "decode_sweep": sweep,
