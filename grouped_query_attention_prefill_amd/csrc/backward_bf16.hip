@@ -402,9 +402,12 @@ bwd_dq_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
 
-  // heaviest query blocks first (as the forward)
-  const int bgh = blockIdx.x / p.n_qblocks;
-  const int qb = p.n_qblocks - 1 - (blockIdx.x % p.n_qblocks);
+  // heaviest query blocks first across every (sequence, K/V head, head chunk): the
+  // dispatcher starts workgroups in grid order, so the long rows of all heads spread
+  // over the chip first and short ones fill in behind them
+  const int n_bgh = p.B * p.h_kv * p.n_hchunks;
+  const int qb = p.n_qblocks - 1 - (int)(blockIdx.x / n_bgh);
+  const int bgh = blockIdx.x % n_bgh;
   const int hc = bgh % p.n_hchunks;
   const int bg = bgh / p.n_hchunks;
   const int g = bg % p.h_kv, b = bg / p.h_kv;
