@@ -26,10 +26,12 @@
 // 8 waves form two groups of four, one wave of each on every SIMD, and the second
 // group runs one phase behind the first: while one wave of a SIMD keeps the matrix
 // core busy, the other does its exponentials, and a workgroup barrier between
-// phases keeps the two groups in step.  The leading group stages the tiles: early
-// in its matrix phase t it requests K tile t + 1 and V tile t with buffer loads
-// that write LDS directly (no registers pass them), and it waits for them at the
-// end of its next vector phase, two phases later.  The ROPE instances rotate the
+// phases keeps the two groups in step.  The trailing group stages the tiles: at
+// the start of its vector phase, while the leading group's matrix phase t runs, it
+// requests K tile t + 1 and V tile t with buffer loads that write LDS directly (no
+// registers pass them), and it waits for them at the end of its next matrix phase,
+// before their first reader; the leading group's matrix phases carry no load
+// instructions.  The ROPE instances rotate the
 // workgroup's Q rows at their positions (in LDS, before any tile is loaded).  O is
 // written through LDS as whole 128-byte lines with the non-temporal hint.
 //
@@ -120,6 +122,16 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier after a vector phase: that phase reads and writes no LDS, so no
+// wait precedes the barrier (the same compiler and scheduler fences as above).
+__device__ __forceinline__ void vector_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -270,8 +282,8 @@ prefill_bf16_kernel(PrefillParams p) {
   f32x16 sacc[4];
 
   // ---- staging: K and V tiles straight from memory into their stages, all requested
-  // by the leading group.  Tile t of the (b, g) slice goes to stage t & 1; 1 KiB block j
-  // of a stage is written by leading wave j % 4.  *_off[i] is this lane's byte offset
+  // by the trailing group.  Tile t of the (b, g) slice goes to stage t & 1; 1 KiB block j
+  // of a stage is written by trailing wave j % 4.  *_off[i] is this lane's byte offset
   // within a tile for block gw + 4 i.  Keys at or past kv_end read as zeros (the
   // descriptors' range ends there); a lane whose 16 bytes are row padding reads at
   // 2^31, past any range the API admits (a head's slice is below 2^31 bytes), so it
@@ -309,19 +321,14 @@ prefill_bf16_kernel(PrefillParams p) {
   auto k_stage = [&](const int t) { return lds + (t & 1) * L::K_STAGE; };
   auto v_stage = [&](const int t) { return lds + L::V_OFF + (t & 1) * L::V_STAGE; };
 
-  // ---- matrix phase t: O^T += V^T P^T for tile t - 1 (PV) and S^T = K Q^T for tile t
-  // (QK), in PhaseOrder.  Operand reads run kWin products ahead of the products that
-  // consume them, in an order pinned by scheduling barriers.  After product kLoadAt the
-  // leading group requests K tile t + 1 (into kdst) and V tile t (into vdst), stages no
-  // wave reads before the barrier that ends the next phase (see the pipeline below), so
-  // the loads have two phases to land.  The four stage pointers are restrict-qualified
-  // because they never overlap; that also tells the compiler that the phase's LDS reads
-  // need not wait for the loads just requested.
+  // ---- matrix phase: O^T += V^T P^T for the previous tile (PV, V stage vs_) and
+  // S^T = K Q^T for this one (QK, K stage ks_), in PhaseOrder.  Operand reads run kWin
+  // products ahead of the products that consume them, in an order pinned by
+  // scheduling barriers.  The stages read here are never the ones the trailing
+  // group's loads in flight are writing (see the pipeline below).
   constexpr int kWin = 8;
-  constexpr int kLoadAt = 1;
   bf16x8 ops[kWin];
-  auto matrix_phase = [&](const int t, auto qk_tag, auto pv_tag, unsigned char* __restrict__ kdst,
-                          unsigned char* __restrict__ vdst, const unsigned char* __restrict__ ks_,
+  auto matrix_phase = [&](auto qk_tag, auto pv_tag, const unsigned char* __restrict__ ks_,
                           const unsigned char* __restrict__ vs_) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
@@ -350,19 +357,18 @@ prefill_bf16_kernel(PrefillParams p) {
         sacc[x] = mfma32(ops[j % kWin], qf[y], y == 0 ? f32x16{} : sacc[x]);
       }
       if (j + kWin < N) ops[j % kWin] = read(j + kWin);
-      if (QK && j == kLoadAt) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (grp == 0) {
-          if (t + 1 < n_tiles) load_k_tile(kdst, t + 1);
-          load_v_tile(vdst, t);
-        }
-      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- vector phase t: online-softmax update from S^T of tile t; P^T packed in place
+  // ---- vector phase t: online-softmax update from S^T of tile t; P^T packed in place.
+  // The trailing group first requests K tile t + 2 and V tile t + 1 (the leading
+  // group is then in its matrix phase t + 1).
   auto vector_phase = [&](const int t) {
+    if (grp == 1) {
+      if (t + 2 < n_tiles) load_k_tile(k_stage(t + 2), t + 2);
+      if (t + 1 < n_tiles) load_v_tile(v_stage(t + 1), t + 1);
+    }
     const int k0 = t * kTile;
     // mask only where some key of the tile may be invisible to some row
     const bool need_mask = (p.causal && k0 + kTile - 1 > min_pos) || (k0 + kTile > len_b);
@@ -416,34 +422,40 @@ prefill_bf16_kernel(PrefillParams p) {
 
   // ---- pipeline.  Slot 2t: leading group matrix phase t, trailing group vector phase
   // t - 1; slot 2t + 1: leading vector t, trailing matrix t; a workgroup barrier ends
-  // every slot.  Matrix phase t reads K tile t and V tile t - 1.  Early in slot 2t the
-  // leading group requests K tile t + 1, into the stage of K tile t - 1 (last read in
-  // slot 2t - 1), and V tile t, into the stage of V tile t - 2 (last read in slot
-  // 2t - 1); it waits for both at the end of slot 2t + 1, before their first reader.
-  // (Phases without QK products request nothing; their unused destination pointers
-  // only keep the four stages distinct.)
+  // every slot.  Matrix phase t reads K tile t and V tile t - 1.  At the start of slot
+  // 2t the trailing group requests K tile t + 1, into the stage of K tile t - 1 (last
+  // read in slot 2t - 1), and V tile t, into the stage of V tile t - 2 (last read in
+  // slot 2t - 1); its matrix phase t in slot 2t + 1 reads neither of those stages, and
+  // it waits for the loads at the end of that phase, before their first reader (the
+  // leading group's matrix phase t + 1).  The barrier after a matrix phase waits for
+  // this wave's LDS reads; the one after a vector phase, which touches no LDS, waits
+  // for nothing.
   if (n_tiles > 0) {
     const auto yes = std::integral_constant<bool, true>{};
     const auto no = std::integral_constant<bool, false>{};
     if constexpr (ROPE) load_q_rotated();
-    if (grp == 0) load_k_tile(k_stage(0), 0);
+    if (grp == 1) load_k_tile(k_stage(0), 0);
     wait_lds_loads();               // K tile 0, and every wave's Q fragments
     stage_barrier();
-    if (grp == 1) stage_barrier();  // the trailing group starts one phase late
-    matrix_phase(0, yes, no, k_stage(1), v_stage(0), k_stage(0), v_stage(1));
-    stage_barrier();
-    vector_phase(0);
-    if (grp == 0) wait_lds_loads(); // K tile 1, V tile 0
-    stage_barrier();
-    for (int t = 1; t < n_tiles; ++t) {
-      matrix_phase(t, yes, yes, k_stage(t + 1), v_stage(t), k_stage(t), v_stage(t - 1));
-      stage_barrier();
-      vector_phase(t);
-      if (grp == 0) wait_lds_loads();   // K tile t + 1, V tile t
+    if (grp == 1) {
+      // the trailing group starts one phase late; it requests K tile 1 and V tile 0
+      if (1 < n_tiles) load_k_tile(k_stage(1), 1);
+      load_v_tile(v_stage(0), 0);
       stage_barrier();
     }
-    matrix_phase(n_tiles, no, yes, k_stage(n_tiles + 1), v_stage(n_tiles), k_stage(n_tiles),
-                 v_stage(n_tiles - 1));
+    matrix_phase(yes, no, k_stage(0), v_stage(1));
+    if (grp == 1) wait_lds_loads();
+    stage_barrier();
+    vector_phase(0);
+    vector_barrier();
+    for (int t = 1; t < n_tiles; ++t) {
+      matrix_phase(yes, yes, k_stage(t), v_stage(t - 1));
+      if (grp == 1) wait_lds_loads();   // K tile t + 1, V tile t
+      stage_barrier();
+      vector_phase(t);
+      vector_barrier();
+    }
+    matrix_phase(no, yes, k_stage(n_tiles), v_stage(n_tiles - 1));
     if (grp == 0) stage_barrier();  // pairs with the trailing group's last barrier
   }
 
