@@ -79,7 +79,8 @@ struct PrefillParams {
 // LDS: two K stages, then two V stages, each a 128-key tile with padded rows.  The
 // stages are filled by buffer loads that write LDS directly, 1 KiB per instruction
 // (64 lanes x 16 bytes, lane i at byte 16 i); a lane whose 16 bytes fall in a row's
-// padding is switched off, so the padding is never written.
+// padding reads outside its descriptor's range, so it touches no memory and writes
+// zeros into padding that no product reads.
 template <int D>
 struct PrefillLds {
   static constexpr int KS = D * 2 + 16;          // K row stride, bytes
