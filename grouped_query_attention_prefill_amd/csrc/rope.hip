@@ -34,9 +34,9 @@ struct Vec<T, 1> { typedef T type; };
 
 // One thread per (row, VEC consecutive pairs).  Rows are (b, h, s) of a (B, H, S, d)
 // tensor; row s of sequence b sits at position pos0[b] + s.  With VEC > 1 both halves
-// of the pairs move as 16-byte vectors.
-// One launch may rotate two tensors of the same rows' positions (Q and K): chunk
-// indices past the first tensor's fall to the second.
+// of the pairs move as 16-byte vectors (the launcher uses rope_heads_kernel below for
+// those).  One launch may rotate two tensors of the same rows' positions (Q and K):
+// chunk indices past the first tensor's fall to the second.
 struct RopeSeg {
   const void* x;
   void* y;
@@ -79,6 +79,69 @@ rope_kernel(RopeSeg a, RopeSeg a2, const int32_t* pos0, int S, int half, RopeFre
   }
   *reinterpret_cast<V*>(yr) = lo;
   *reinterpret_cast<V*>(yr + half) = hi;
+}
+
+// The vectorized form: one thread per (sequence, group of kHeadGroup heads, position,
+// VEC consecutive pairs).  The angles depend only on the position and the pair, so a
+// thread computes its VEC sines and cosines once and turns the same pairs of every
+// head of its group; it requests all of the group's rows before it turns any, so
+// 2 kHeadGroup 16-byte loads are in flight per thread.  Consecutive threads take
+// consecutive pairs, then positions, so each head's rows are read and written as
+// contiguous runs.  The arithmetic per element is the one above, bit for bit.
+constexpr int kHeadGroup = 8;
+
+template <typename T, int VEC>
+__global__ void __launch_bounds__(256)
+rope_heads_kernel(RopeSeg a, RopeSeg a2, long long n1, long long n2, const int32_t* pos0, int S, int half,
+                  RopeFreq f) {
+  typedef typename Vec<T, VEC>::type V;
+  long long cidx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const bool second = cidx >= n1;
+  if (second) {
+    cidx -= n1;
+    if (cidx >= n2) return;
+  }
+  const T* x = static_cast<const T*>(second ? a2.x : a.x);
+  T* y = static_cast<T*>(second ? a2.y : a.y);
+  const int H = second ? a2.H : a.H;
+  const int n_groups = (H + kHeadGroup - 1) / kHeadGroup;
+  const int chunks = half / VEC;
+  const int i0 = (int)(cidx % chunks) * VEC;
+  long long rest = cidx / chunks;
+  const int s = (int)(rest % S);
+  rest /= S;
+  const int grp = (int)(rest % n_groups);
+  const int b = (int)(rest / n_groups);
+  const int p = (pos0 ? pos0[b] : 0) + s;
+  const int h0 = grp * kHeadGroup;
+  const int nh = min(kHeadGroup, H - h0);
+  const long long row_stride = (long long)S * 2 * half;        // elements between heads
+  const long long base = ((long long)(b * H + h0) * S + s) * 2 * half + i0;
+  V lo[kHeadGroup], hi[kHeadGroup];
+#pragma unroll
+  for (int j = 0; j < kHeadGroup; ++j)
+    if (j < nh) {
+      lo[j] = *reinterpret_cast<const V*>(x + base + j * row_stride);
+      hi[j] = *reinterpret_cast<const V*>(x + base + j * row_stride + half);
+    }
+  float c[VEC], sn[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) rope_cos_sin(p, f.turn_frac[i0 + v], c[v], sn[v]);
+#pragma unroll
+  for (int j = 0; j < kHeadGroup; ++j)
+    if (j < nh) {
+      T* l = reinterpret_cast<T*>(&lo[j]);
+      T* u = reinterpret_cast<T*>(&hi[j]);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        float y0, y1;
+        rope_rotate(ld(l + v), ld(u + v), c[v], sn[v], y0, y1);
+        st(l + v, y0);
+        st(u + v, y1);
+      }
+      *reinterpret_cast<V*>(y + base + j * row_stride) = lo[j];
+      *reinterpret_cast<V*>(y + base + j * row_stride + half) = hi[j];
+    }
 }
 
 // Append with the key rotated at its own position: one workgroup per (K/V head,
@@ -126,16 +189,26 @@ hipError_t launch_rope_pair(const void* x, void* y, int H, const void* x2, void*
   const int vec = !al16 ? 1 : (elem_bytes == 4 ? (half % 4 == 0 ? 4 : 1) : (half % 8 == 0 ? 8 : 1));
   const RopeSeg a{x, y, H, (long long)B * H * S * (half / vec)};
   const RopeSeg a2{x2, y2, H2, (long long)B * H2 * S * (half / vec)};
+  if (vec > 1) {
+    // head groups: each thread turns the same pairs of up to kHeadGroup heads
+    const long long n1 = (long long)B * ((H + kHeadGroup - 1) / kHeadGroup) * S * (half / vec);
+    const long long n2 = (long long)B * ((H2 + kHeadGroup - 1) / kHeadGroup) * S * (half / vec);
+    const long long blocks = (n1 + n2 + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (blocks == 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (elem_bytes == 4)
+      hipLaunchKernelGGL((rope_heads_kernel<float, 4>), grid, block, 0, s, a, a2, n1, n2, pos0, S, half, f);
+    else
+      hipLaunchKernelGGL((rope_heads_kernel<uint16_t, 8>), grid, block, 0, s, a, a2, n1, n2, pos0, S, half, f);
+    return hipGetLastError();
+  }
+  // element by element (unaligned tensors, or half widths the vectors do not divide)
   const long long blocks = (a.n_chunks + a2.n_chunks + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
-  if (elem_bytes == 4) {
-    if (vec == 4) hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, 0, s, a, a2, pos0, S, half, f);
-    else hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, 0, s, a, a2, pos0, S, half, f);
-  } else {
-    if (vec == 8) hipLaunchKernelGGL((rope_kernel<uint16_t, 8>), grid, block, 0, s, a, a2, pos0, S, half, f);
-    else hipLaunchKernelGGL((rope_kernel<uint16_t, 1>), grid, block, 0, s, a, a2, pos0, S, half, f);
-  }
+  if (elem_bytes == 4) hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, 0, s, a, a2, pos0, S, half, f);
+  else hipLaunchKernelGGL((rope_kernel<uint16_t, 1>), grid, block, 0, s, a, a2, pos0, S, half, f);
   return hipGetLastError();
 }
 
