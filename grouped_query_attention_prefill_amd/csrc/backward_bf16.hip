@@ -25,8 +25,10 @@
 //     add their partial sums at the end.
 //   dQ: a workgroup owns 128 query rows (heads x positions of one group, as in
 //     the forward); Q and dO rows stay in registers and 64-key tiles of K and V
-//     stream through LDS, each worked in two 32-key halves (S^T = K Q^T,
-//     dP^T = V dO^T, dQ^T += K^T dS^T) so that two workgroups fit a CU.
+//     reach LDS through buffer loads that write it directly (double-buffered,
+//     the next tile requested as a tile's work starts), each worked in two 32-key
+//     halves (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T) so that two
+//     workgroups fit a CU.
 #include <type_traits>
 
 #include "internal.h"
@@ -390,7 +392,19 @@ struct DqLds {
   static constexpr int K_BYTES = kDqTile * KTS;
   static constexpr int STAGE = K_BYTES + kDqTile * VTS;
   static constexpr int TOTAL = 2 * STAGE;
+  static constexpr int K_BLOCKS = K_BYTES / 1024;                  // 1 KiB load blocks per stage
+  static constexpr int V_BLOCKS = kDqTile * VTS / 1024;
+  static constexpr int MAXB = (K_BLOCKS + 3) / 4;                  // blocks per wave and tensor
+  static_assert(K_BYTES % 1024 == 0 && (kDqTile * VTS) % 1024 == 0, "stages are whole 1 KiB blocks");
+  static_assert(K_BLOCKS >= V_BLOCKS, "the K part is the larger");
 };
+
+// One 16-byte-per-lane buffer load written straight into LDS: lane i's 16 bytes from
+// byte voff + soff of the descriptor's range land at dst + 16 i (dst wave-uniform).
+__device__ __forceinline__ void bwd_load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t voff,
+                                               uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
 
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 2)
@@ -453,41 +467,57 @@ bwd_dq_kernel(BwdParams p) {
   const uint32_t slice = (uint32_t)kv_end * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_base, slice);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice);
-  constexpr int UNITS = kDqTile * D / 8 / kBwdThreads;
-  uint4 kreg[UNITS], vreg[UNITS];
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
+  // ---- staging: K and V tiles straight from memory into their stages with buffer
+  // loads that write LDS directly.  1 KiB block j of a stage's K (V) part is written by
+  // wave j % 4; *_off[i] is this lane's byte offset within a tile for block wave + 4 i.
+  // Keys at or past kv_end read as zeros (the descriptors' range ends there); a lane
+  // whose 16 bytes are row padding reads at 2^31, outside any range the API admits, so
+  // it touches no memory and writes zeros into padding no product reads.
+  uint32_t k_off[L::MAXB], v_off[L::MAXB];
 #pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      const int u = tid + kBwdThreads * i;
-      const int row = u / (D / 8), c8 = u % (D / 8);
-      const uint32_t off = (uint32_t)((t * kDqTile + row) * D + c8 * 8) * 2;
-      kreg[i] = load16(krs, off);
-      vreg[i] = load16(vrs, off);
-    }
-  };
-  auto store_tile = [&](int stage) __attribute__((always_inline)) {
-    unsigned char* ks_ = lds + stage * L::STAGE;
-    unsigned char* vs_ = ks_ + L::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      const int u = tid + kBwdThreads * i;
-      const int row = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<uint4*>(ks_ + row * L::KTS + c8 * 16) = kreg[i];
-      *reinterpret_cast<uint4*>(vs_ + row * L::VTS + c8 * 16) = vreg[i];
-    }
-  };
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  for (int i = 0; i < L::MAXB; ++i) {
+    const int a = (wave + 4 * i) * 1024 + lane * 16;
+    const int rk = a / L::KTS, ok = a - rk * L::KTS;
+    const int rv = a / L::VTS, ov = a - rv * L::VTS;
+    k_off[i] = ok < D * 2 ? (uint32_t)(rk * D * 2 + ok) : 0x80000000u;
+    v_off[i] = ov < D * 2 ? (uint32_t)(rv * D * 2 + ov) : 0x80000000u;
   }
-  for (int t = 0; t < n_tiles; ++t) {
-    const int set = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    lds_barrier();
-    const unsigned char* ks_ = lds + set * L::STAGE;
-    const unsigned char* vs_ = ks_ + L::K_BYTES;
+  auto load_tile = [&](unsigned char* __restrict__ stage, int t) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)t * kDqTile * D * 2;
+#pragma unroll
+    for (int i = 0; i < L::MAXB; ++i) {
+      if (wave + 4 * i < L::K_BLOCKS) bwd_load_lds16(krs, stage + (wave + 4 * i) * 1024, k_off[i], soff);
+      if (wave + 4 * i < L::V_BLOCKS)
+        bwd_load_lds16(vrs, stage + L::K_BYTES + (wave + 4 * i) * 1024, v_off[i], soff);
+    }
+  };
+  auto wait_loads = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads into LDS have landed
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Workgroup barrier that does not wait for loads still in flight (a release fence
+  // would): lgkmcnt(0) completes this wave's LDS reads; the empty asm statements keep
+  // the compiler from moving memory accesses across it.
+  auto tile_barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Tile t on its stage; `next` (the other stage, free since the last barrier) first
+  // receives tile t + 1.  The pointers are restrict-qualified because they never
+  // overlap; that also tells the compiler the reads of `cur` need not wait for the
+  // loads into `next`.
+  auto tile_work = [&](const int t, unsigned char* __restrict__ next, const unsigned char* __restrict__ cur)
+      __attribute__((always_inline)) {
+    if (t + 1 < n_tiles) load_tile(next, t + 1);
+    const unsigned char* ks_ = cur;
+    const unsigned char* vs_ = cur + L::K_BYTES;
     const int k0 = t * kDqTile;
-    const bool edge = (p.causal && k0 + kDqTile - 1 > first_q) || (k0 + kDqTile > len_b);
+    const bool edge = (causal && k0 + kDqTile - 1 > first_q) || (k0 + kDqTile > len_b);
     // the tile in two 32-key halves, each: S^T, dP^T, dS^T, then its two 16-key chunks of dQ^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -516,20 +546,30 @@ bwd_dq_kernel(BwdParams p) {
       else grads(std::false_type{});
       bf16x8 dsf[2];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int e0 = 8 * c2;
-        dsf[c2] = pack_bf16x8(dpacc[e0], dpacc[e0 + 1], dpacc[e0 + 2], dpacc[e0 + 3], dpacc[e0 + 4], dpacc[e0 + 5],
-                              dpacc[e0 + 6], dpacc[e0 + 7]);
+      for (int c2_ = 0; c2_ < 2; ++c2_) {
+        const int e0 = 8 * c2_;
+        dsf[c2_] = pack_bf16x8(dpacc[e0], dpacc[e0 + 1], dpacc[e0 + 2], dpacc[e0 + 3], dpacc[e0 + 4],
+                               dpacc[e0 + 5], dpacc[e0 + 6], dpacc[e0 + 7]);
       }
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
+      for (int c2_ = 0; c2_ < 2; ++c2_)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 a = load_vt_operand(ks_, L::KTS, 2 * kb + c2, db * 32, lane);
-          dqacc[db] = mfma32(a, dsf[c2], dqacc[db]);
+          const bf16x8 a = load_vt_operand(ks_, L::KTS, 2 * kb + c2_, db * 32, lane);
+          dqacc[db] = mfma32(a, dsf[c2_], dqacc[db]);
         }
     }
-    if (t + 1 < n_tiles) store_tile(set ^ 1);
+  };
+  auto stage_at = [&](int t) { return lds + (t & 1) * L::STAGE; };
+  if (n_tiles > 0) {
+    load_tile(stage_at(0), 0);
+    wait_loads();
+    tile_barrier();
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    tile_work(t, stage_at(t + 1), stage_at(t));
+    wait_loads();                 // tile t + 1 has landed in this wave's blocks
+    tile_barrier();               // ... in every wave's; and every wave is done with tile t
   }
 
   if (row_valid) {
