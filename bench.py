@@ -401,7 +401,46 @@ def bench_decode(name, steps, warmup, flush_buf, page_size=0):
         res["page_size"] = page_size
     del qd, kd, vd, out, ws, bt
     torch.cuda.empty_cache()
+    res["read_floor"] = read_floor(nbytes, steps, warmup, flush, kern_ms)
     return res, x
+
+
+_FLOOR_LIB = None
+
+
+def read_floor(nbytes, steps, warmup, flush, row_ms):
+    """Time one streaming read of nbytes (libgqa_readfloor.so) the way a decode row is
+    timed: inputs evicted from the Infinity Cache, HIP events around each call.  The
+    row's time over this floor says how far the row is from what reading its bytes
+    once costs on this GPU."""
+    import ctypes
+    import os
+
+    import torch
+
+    global _FLOOR_LIB
+    if _FLOOR_LIB is None:
+        path = os.path.join(ROOT, "grouped_query_attention_prefill_amd", "libgqa_readfloor.so")
+        lib = ctypes.CDLL(path)
+        lib.gqa_read_floor.restype = ctypes.c_int
+        lib.gqa_read_floor.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gqa_read_floor_grid.restype = ctypes.c_int
+        _FLOOR_LIB = lib
+    lib = _FLOOR_LIB
+    n = (nbytes + 15) // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty(max(lib.gqa_read_floor_grid(), 1), dtype=torch.int32, device="cuda")
+
+    def fn():
+        st = lib.gqa_read_floor(buf.data_ptr(), n, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0, "gqa_read_floor failed"
+
+    _, per = time_calls(fn, steps, warmup, flush=flush)
+    ms = sum(per) / len(per)
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"kernel": "streaming read of the row's algorithmic bytes", "ms_per_call": round(ms, 5),
+            "GB/s": round(n / (ms * 1e-3) / 1e9, 1), "row_over_floor": round(row_ms / ms, 3)}
 
 
 # ---------------------------------------------------------------------------------------- backward

@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
+# the benchmark's streaming-read reference kernel, kept out of the attention library
+FLOOR_SRC = "read_floor.hip"
+FLOOR_LIB = os.path.join(PKG, "libgqa_readfloor.so")
 
 SOURCES = ["api.hip", "attn_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "kv_append.hip", "rope.hip", "backward_bf16.hip"]
 ARCH = "gfx950"
@@ -48,18 +51,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [FLOOR_SRC]))
+    _link(objs[:-1], LIB, verbose)
+    _link(objs[-1:], FLOOR_LIB, verbose)
     return LIB
 
 

@@ -68,6 +68,14 @@ def trace_summary(out_dir: str, last: int = 20) -> str:
         for part in line.get("decode_sweep", []):
             lines.append(f"* {part['workload']}: ms_per_call = {part['ms_per_call']}, {part['value']} "
                          f"{part['unit']}, roofline frac {part['roofline']['frac']}")
+        floors = [p_ for p_ in [line.get("decode")] + line.get("decode_sweep", []) if p_ and p_.get("read_floor")]
+        if floors:
+            lines += ["", "Streaming-read floor of each decode row (the row's algorithmic bytes read once, timed "
+                      "the same way):", ""]
+            for part in floors:
+                f_ = part["read_floor"]
+                lines.append(f"* {part['workload']}: floor {f_['ms_per_call']} ms ({f_['GB/s']} GB/s), "
+                             f"row / floor = {f_['row_over_floor']}")
     return "\n".join(lines) + "\n"
 
 
