@@ -55,7 +55,7 @@ TRAFFIC_ROWS = {
     **{(n + (f"_paged{ps}" if ps else "")): (["--only", "sweep", "--workload", n + (f":{ps}" if ps else "")],
                                              ("decode_main", "mean"), ["decode_bf16.hip", "rope_common.h", *_COMMON])
        for n, ps in SWEEP},
-    "prefill_causal_bf16_T4096_qk_rope": (["--only", "rope"], ("rope_kernel", "largest_grid"),
+    "prefill_causal_bf16_T4096_qk_rope": (["--only", "rope"], ("rope_heads_kernel", "largest_grid"),
                                           ["rope.hip", "rope_common.h", "internal.h"]),
     "prefill_causal_bf16_T4096_backward": (["--only", "backward"],
                                            (("bwd_delta", "bwd_dkdv_kernel", "bwd_dq_kernel"), "sum_of_means"),

@@ -39,7 +39,7 @@ def _counter_rows(counter, dispatches):
 PREFILL = "void gqa::(anonymous namespace)::prefill_bf16_kernel<128, false, false>(gqa::PrefillParams)"
 DECODE = "void gqa::(anonymous namespace)::decode16_bf16_kernel<128, false, false>(gqa::DecodeParams)"
 COMBINE = "void gqa::(anonymous namespace)::decode_combine_kernel<128, false>(gqa::DecodeParams)"
-ROPE = "void gqa::(anonymous namespace)::rope_kernel<unsigned short, 8>(gqa::RopeParams)"
+ROPE = "void gqa::(anonymous namespace)::rope_heads_kernel<unsigned short, 8>(gqa::(anonymous namespace)::RopeSeg)"
 BWD = ["void gqa::(anonymous namespace)::bwd_delta_vec_kernel<128, false>(gqa::BwdParams)",
        "void gqa::(anonymous namespace)::bwd_dkdv_kernel<128>(gqa::BwdParams)",
        "void gqa::(anonymous namespace)::bwd_dq_kernel<128>(gqa::BwdParams)"]
