@@ -374,14 +374,15 @@ prefill_bf16_kernel(PrefillParams p) {
     // mask only where some key of the tile may be invisible to some row
     const bool need_mask = (p.causal && k0 + kTile - 1 > min_pos) || (k0 + kTile > len_b);
     if (need_mask) {
+      // key k0 + kb * 32 + 8 (e / 4) + 4 h + e % 4 is visible iff it lies below
+      // min(len_b, pos + 1) (causal) or len_b; lim moves k0 + 4 h to that side, so each
+      // element takes one compare against a constant and one select
+      const int lim = (p.causal ? min(len_b, pos + 1) : len_b) - k0 - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          const bool vis = key < len_b && (!p.causal || key <= pos);
-          sacc[kb][e] = vis ? sacc[kb][e] : -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          sacc[kb][e] = (kb * 32 + 8 * (e >> 2) + (e & 3)) < lim ? sacc[kb][e] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
