@@ -42,8 +42,9 @@ int gqa_read_floor_grid(void) {
 // Read bytes (a multiple of 16) of device buffer x once on `stream`; out: device buffer of
 // gqa_read_floor_grid() unsigned words.  Returns 0, or 1 on a bad argument or launch error.
 int gqa_read_floor(const void* x, size_t bytes, unsigned* out, void* stream) {
+  if (!x || !out || bytes % 16 != 0) return 1;   // checked before any HIP call
   const int grid = gqa_read_floor_grid();
-  if (!x || !out || bytes % 16 != 0 || grid < 1) return 1;
+  if (grid < 1) return 1;
   hipLaunchKernelGGL(read_floor_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(x), bytes / 16, out);
   return hipGetLastError() == hipSuccess ? 0 : 1;
