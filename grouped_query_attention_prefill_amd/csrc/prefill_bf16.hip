@@ -26,12 +26,12 @@
 // 8 waves form two groups of four, one wave of each on every SIMD, and the second
 // group runs one phase behind the first: while one wave of a SIMD keeps the matrix
 // core busy, the other does its exponentials, and a workgroup barrier between
-// phases keeps the two groups in step.  The trailing group stages the tiles: at
-// the start of its vector phase, while the leading group's matrix phase t runs, it
-// requests K tile t + 1 and V tile t with buffer loads that write LDS directly (no
-// registers pass them), and it waits for them at the end of its next matrix phase,
-// before their first reader; the leading group's matrix phases carry no load
-// instructions.  The ROPE instances rotate the
+// phases keeps the two groups in step.  The trailing group stages the tiles: during
+// its vector phase, while the leading group's matrix phase t runs, it requests K
+// tile t + 1 and V tile t with buffer loads that write LDS directly (no registers
+// pass them), each wave at its own point of the phase, and it waits for them at the
+// end of its next matrix phase, before their first reader; the leading group's
+// matrix phases carry no load instructions.  The ROPE instances rotate the
 // workgroup's Q rows at their positions (in LDS, before any tile is loaded).  O is
 // written through LDS as whole 128-byte lines with the non-temporal hint.
 //
@@ -363,13 +363,20 @@ prefill_bf16_kernel(PrefillParams p) {
   };
 
   // ---- vector phase t: online-softmax update from S^T of tile t; P^T packed in place.
-  // The trailing group first requests K tile t + 2 and V tile t + 1 (the leading
-  // group is then in its matrix phase t + 1).
+  // The trailing group also requests K tile t + 2 and V tile t + 1 (the leading group
+  // is then in its matrix phase t + 1).
   auto vector_phase = [&](const int t) {
-    if (grp == 1) {
-      if (t + 2 < n_tiles) load_k_tile(k_stage(t + 2), t + 2);
-      if (t + 1 < n_tiles) load_v_tile(v_stage(t + 1), t + 1);
-    }
+    // Trailing wave gw requests its blocks of both tiles at point gw of the phase (the
+    // start, after the maximum, after the first and the second block of exponentials),
+    // so that one wave's loads at a time queue in the memory pipeline: a wave's later
+    // instructions wait until its own loads are taken, and the other three compute.
+    auto loads_at = [&](const int point) {
+      if (grp == 1 && gw == point) {
+        if (t + 2 < n_tiles) load_k_tile(k_stage(t + 2), t + 2);
+        if (t + 1 < n_tiles) load_v_tile(v_stage(t + 1), t + 1);
+      }
+    };
+    loads_at(0);
     const int k0 = t * kTile;
     // mask only where some key of the tile may be invisible to some row
     const bool need_mask = (p.causal && k0 + kTile - 1 > min_pos) || (k0 + kTile > len_b);
@@ -390,6 +397,8 @@ prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = pair_max(mx);
+    asm volatile("" : "+v"(mx));
+    loads_at(1);
     // move the running maximum only when it grew by more than 2^kLazyRescale
     const bool grow = (mx - m_run) * p.c > kLazyRescale;     // false for -inf - (-inf)
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -415,7 +424,13 @@ prefill_bf16_kernel(PrefillParams p) {
       const bf16x8 c0 = pack_bf16x8(sv[0], sv[1], sv[2], sv[3], sv[4], sv[5], sv[6], sv[7]);
       const bf16x8 c1 = pack_bf16x8(sv[8], sv[9], sv[10], sv[11], sv[12], sv[13], sv[14], sv[15]);
       typedef float f32x4_ __attribute__((ext_vector_type(4)));
-      const f32x4_ w0 = __builtin_bit_cast(f32x4_, c0), w1 = __builtin_bit_cast(f32x4_, c1);
+      f32x4_ w0 = __builtin_bit_cast(f32x4_, c0), w1 = __builtin_bit_cast(f32x4_, c1);
+      if (kb < 2) {
+        // block kb's exponentials come before the loads of point kb + 2 (the empty asm
+        // keeps the compiler from moving them past the loads)
+        asm volatile("" : "+v"(w0), "+v"(w1), "+v"(psum));
+        loads_at(kb + 2);
+      }
       sv[0] = w0[0]; sv[1] = w0[1]; sv[2] = w0[2]; sv[3] = w0[3];
       sv[4] = w1[0]; sv[5] = w1[1]; sv[6] = w1[2]; sv[7] = w1[3];
     }
