@@ -58,7 +58,7 @@ TRAFFIC_ROWS = {
     "prefill_causal_bf16_T4096_qk_rope": (["--only", "rope"], ("rope_heads_kernel", "largest_grid"),
                                           ["rope.hip", "rope_common.h", "internal.h"]),
     "prefill_causal_bf16_T4096_backward": (["--only", "backward"],
-                                           (("bwd_delta", "bwd_dkdv_kernel", "bwd_dq_kernel"), "sum_of_means"),
+                                           (("bwd_delta", "bwd_dkdv", "bwd_dq_kernel"), "sum_of_means"),
                                            ["backward_bf16.hip", *_COMMON]),
 }
 COPY_ROW = (["--only", "copy"], ("copyBuffer", "mean"))

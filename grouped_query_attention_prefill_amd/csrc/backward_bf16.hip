@@ -16,13 +16,15 @@
 // depend on scheduling.
 //
 // Two kernels recompute the probabilities independently:
-//   dK/dV: a workgroup owns 64 keys of one (sequence, K/V head); each wave owns
-//     32 of them, their K and V rows held in registers, and walks the 32-row query
-//     tiles of every query head in the group that can see those keys.  Per tile:
+//   dK/dV: a workgroup owns 64 keys of one (sequence, K/V head) and walks the
+//     32-row query tiles of every query head in the group that can see those keys;
+//     each wave's keys have their K and V rows in registers.  Per tile:
 //     S = Q K^T and dP = dO V^T (rows = queries, one key per lane column), then
 //     dV^T += dO^T P and dK^T += Q^T dS with P and dS straight from registers and
-//     dO^T, Q^T read transposed from LDS.  Waves of the two query-tile parities
-//     add their partial sums at the end.
+//     dO^T, Q^T read transposed from LDS.  Waves of different query-tile parities
+//     add their partial sums at the end.  Head width 128 runs 16 keys per wave on
+//     16x16x32 products, three waves per SIMD (bwd_dkdv16_kernel); head width 64
+//     runs 32 keys per wave on 32x32x16 products, one wave per SIMD.
 //   dQ: a workgroup owns 128 query rows (heads x positions of one group, as in
 //     the forward); Q and dO rows stay in registers and 64-key tiles of K and V
 //     reach LDS through buffer loads that write it directly (double-buffered,
@@ -385,6 +387,300 @@ bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK/dV for head width 128 on 16x16x32 products, three waves per SIMD.  A
+// workgroup owns 64 keys of one (sequence, K/V head); its 12 waves are 4 key
+// quarters (16 keys each, K and V rows in registers) x 3 query-tile parities.  The
+// Q and dO tiles of a parity's item (32 rows of one query head) reach LDS through
+// buffer loads that write it directly, two items ahead (three stages per parity),
+// and serve the parity's four waves.  16 keys per wave keep the dK^T and dV^T
+// accumulators at 64 registers, so the kernel fits 170 registers and three waves
+// share each SIMD.  Per item and wave:
+//     S, dP (32 rows x 16 keys)   A: Q / dO rows from LDS, B: K / V fragments
+//     dV^T, dK^T (128 d x 16 keys) += dO^T P, Q^T dS   A: transposing LDS reads,
+//                                                      B: P / dS from registers
+// 16x16x32 lane layouts: A (16 x 32) lane l holds A[l % 16][8 (l / 16) + t];
+// B (32 x 16) lane l holds B[8 (l / 16) + t][l % 16]; C lane l, element j holds
+// C[4 (l / 16) + j][l % 16].  The score block rb (rows 16 rb .. 16 rb + 15) thus
+// hands lane l the rows 16 rb + 4 (l / 16) + j of its key, and slot t of the B
+// operand of the second pair of products is row rowof(l / 16, t) =
+// 4 (l / 16) + t (t < 4) or 16 + 4 (l / 16) + t - 4, the order in which the
+// transposing reads below fetch dO^T and Q^T.
+// Tile rows are 256 bytes with their 16-byte chunks permuted by chunk ^ swz(row),
+// which puts the 16 rows of one chunk that a 16-byte row read takes, and the 8 rows
+// x 32 bytes a half-wave of a transposing read takes, on distinct 16-byte bank
+// groups of a 256-byte row of banks.
+constexpr int kDk16Par = 3;        // query-tile parities (waves per SIMD)
+constexpr int kDk16Threads = 256 * kDk16Par;
+constexpr int kDk16Stages = 3;
+constexpr int kDk16Loads = 5;      // load instructions per wave and item: 2 Q, 2 dO, 1 statistics
+
+struct Dkdv16Lds {
+  static constexpr int TILE = kQTile * 256;
+  static constexpr int STATS = 4 * 256;           // L, delta, and a copy of each
+  static constexpr int STAGE = 2 * TILE + STATS;
+  static constexpr int TOTAL = kDk16Par * kDk16Stages * STAGE;
+  static_assert(4 * 64 * 64 * 4 <= TOTAL, "the reduction of the parities fits");
+};
+
+__device__ __forceinline__ int dk16_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte-per-lane buffer load written straight into LDS: lane i's 16 bytes from
+// byte voff + soff of the descriptor's range land at dst + 16 i (dst wave-uniform).
+__device__ __forceinline__ void bwd_load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t voff,
+                                               uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+// 4 bytes per lane: lane i's dword lands at dst + 4 i
+__device__ __forceinline__ void dk16_load_lds4(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, voff, soff, 0, 0);
+}
+
+// A operand (16 d x 32 rows) of dV^T += dO^T P or dK^T += Q^T dS for d block dblk:
+// two transposing reads; source lane (group G, j, q) points at row 4 G + j (then
+// + 16), columns 16 dblk + 4 q .. + 3, so output lane l receives, as slots
+// 0..3 and 4..7, tile[rowof(l / 16, t)][16 dblk + l % 16].
+__device__ __forceinline__ bf16x8 dk16_tr_operand(const unsigned char* __restrict__ tile, int dblk, int lane) {
+  const int G = lane >> 4, s = lane & 15;
+  const int R = 4 * G + (s >> 2), q = s & 3;
+  const int c = 2 * dblk + (q >> 1);
+  const unsigned char* a = tile + R * 256 + ((c ^ dk16_swz(R)) << 4) + 8 * (q & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 16 * 256));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__global__ void __launch_bounds__(kDk16Threads, 1)
+bwd_dkdv16_kernel(BwdParams p) {
+  constexpr int D = 128;
+  using L = Dkdv16Lds;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = wave & 3;          // key quarter
+  const int qw = wave >> 2;         // query-tile parity
+  const int G = lane >> 4, li = lane & 15;
+  const int T = p.T, h_q = p.h_q, r = p.r, causal = p.causal;
+  const float c2 = p.c;
+  const uint16_t* const qp = p.q;
+  const uint16_t* const dop = p.d_o;
+  const float* const lsep = p.lse;
+  const float* const deltap = p.delta;
+
+  const int n_bg = p.B * p.h_kv;
+  const int kb = blockIdx.x / n_bg;
+  const int bg = blockIdx.x % n_bg;
+  const int g = bg % p.h_kv, b = bg / p.h_kv;
+  const int len_b = clampi(p.kv_lens ? p.kv_lens[b] : p.T, 0, p.T);
+  const int key0 = kb * kKeyBlock + kq * 16;        // first key of this wave
+  const int key = key0 + li;                        // this lane's key
+
+  bf16x8 kf[D / 32], vf[D / 32];
+  {
+    const size_t base = ((size_t)(b * p.h_kv + g) * p.T + key) * D;
+    const bool ok = key < len_b;
+#pragma unroll
+    for (int kd = 0; kd < D / 32; ++kd) {
+      uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+      if (ok) {
+        x = *reinterpret_cast<const uint4*>(p.k + base + kd * 32 + G * 8);
+        y = *reinterpret_cast<const uint4*>(p.v + base + kd * 32 + G * 8);
+      }
+      kf[kd] = __builtin_bit_cast(bf16x8, x);
+      vf[kd] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  f32x4 dkacc[D / 16], dvacc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { dkacc[db][e] = 0.f; dvacc[db][e] = 0.f; }
+
+  const int n_qt = (p.T + kQTile - 1) / kQTile;
+  const int qt0 = (p.causal && kb * kKeyBlock < len_b) ? (kb * kKeyBlock) / kQTile : 0;
+  const int per_head = n_qt - qt0;
+  const int n_items = (kb * kKeyBlock < len_b) ? p.r * per_head : 0;
+  const int n_steps = (n_items + kDk16Par - 1) / kDk16Par;
+
+  // staging: wave kq writes 1 KiB blocks kq and kq + 4 (rows 4 j .. 4 j + 3) of the Q
+  // and the dO tile; lane i of block j fills physical chunk i % 16 of row 4 j + i / 16
+  uint32_t voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 4 * (kq + 4 * i) + (lane >> 4);
+    voff[i] = (uint32_t)(row * 256 + (((lane & 15) ^ dk16_swz(row)) << 4));
+  }
+  const uint32_t svoff = lane < 32 ? (uint32_t)lane * 4 : 0x80000000u;
+  const float* const stat_src = (kq & 1) ? deltap : lsep;
+  auto stage_at = [&](int st) { return lds + (qw * kDk16Stages + st) * L::STAGE; };
+  auto issue = [&](int it, unsigned char* __restrict__ stg) __attribute__((always_inline)) {
+    const bool valid = it < n_items;
+    int head, qt;
+    dkdv_item(valid ? it : 0, g, r, per_head, qt0, head, qt);
+    const size_t rbase = ((size_t)(b * h_q + head) * T) * D;
+    const uint32_t bytes = valid ? (uint32_t)T * D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp + rbase, bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dop + rbase, bytes);
+    const uint32_t soff = (uint32_t)qt * kQTile * D * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      bwd_load_lds16(qr, stg + (kq + 4 * i) * 1024, voff[i], soff);
+      bwd_load_lds16(dr, stg + L::TILE + (kq + 4 * i) * 1024, voff[i], soff);
+    }
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(stat_src + (size_t)(b * h_q + head) * T, valid ? (uint32_t)T * 4 : 0u);
+    dk16_load_lds4(sr, stg + 2 * L::TILE + kq * 256, svoff, (uint32_t)qt * kQTile * 4);
+  };
+
+  auto compute = [&](int it, const unsigned char* __restrict__ stg) __attribute__((always_inline)) {
+    int head, qt;
+    dkdv_item(it, g, r, per_head, qt0, head, qt);
+    (void)head;
+    const unsigned char* qs = stg;
+    const unsigned char* os = stg + L::TILE;
+    const float* lv = reinterpret_cast<const float*>(stg + 2 * L::TILE);
+    const float* dl_ = lv + 64;
+    f32x4 sacc[2], dpacc[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kd = 0; kd < D / 32; ++kd) {
+        const int row = 16 * rb + li;
+        const int off = row * 256 + (((4 * kd + G) ^ dk16_swz(row)) << 4);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qs + off);
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(os + off);
+        sacc[rb] = mfma16(a, kf[kd], kd == 0 ? f32x4{} : sacc[rb]);
+        dpacc[rb] = mfma16(o, vf[kd], kd == 0 ? f32x4{} : dpacc[rb]);
+      }
+    const int q0 = qt * kQTile;
+    const bool edge = (causal && key0 + 15 > q0) || (key0 + 16 > len_b) || (q0 + kQTile > T);
+    float lq[8], dq_[8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lv + 16 * rb + 4 * G);
+      const float4 d4 = *reinterpret_cast<const float4*>(dl_ + 16 * rb + 4 * G);
+      lq[4 * rb] = l4.x; lq[4 * rb + 1] = l4.y; lq[4 * rb + 2] = l4.z; lq[4 * rb + 3] = l4.w;
+      dq_[4 * rb] = d4.x; dq_[4 * rb + 1] = d4.y; dq_[4 * rb + 2] = d4.z; dq_[4 * rb + 3] = d4.w;
+    }
+    auto probs = [&](auto masked_tag) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * rb + j;
+          float arg = fmaf(sacc[rb][j], c2, -lq[e] * kLog2e);
+          if constexpr (decltype(masked_tag)::value) {
+            const int qrow = q0 + 16 * rb + 4 * G + j;
+            const bool vis = (lq[e] != -INFINITY) & (key < len_b) & (qrow < T) & (!causal | (key <= qrow));
+            arg = vis ? arg : -INFINITY;
+          }
+          const float pr = fast_exp2(arg);
+          sacc[rb][j] = pr;
+          dpacc[rb][j] = pr * (dpacc[rb][j] - dq_[e]);
+        }
+    };
+    if (edge) probs(std::true_type{});
+    else probs(std::false_type{});
+    const bf16x8 pf = pack_bf16x8(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3], sacc[1][0], sacc[1][1], sacc[1][2],
+                                  sacc[1][3]);
+    const bf16x8 dsf = pack_bf16x8(dpacc[0][0], dpacc[0][1], dpacc[0][2], dpacc[0][3], dpacc[1][0], dpacc[1][1],
+                                   dpacc[1][2], dpacc[1][3]);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const bf16x8 ot = dk16_tr_operand(os, db, lane);
+      const bf16x8 qt_ = dk16_tr_operand(qs, db, lane);
+      dvacc[db] = mfma16(ot, pf, dvacc[db]);
+      dkacc[db] = mfma16(qt_, dsf, dkacc[db]);
+    }
+  };
+
+  auto step_barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // vmcnt(kDk16Loads): all but the loads of the last item issued have landed
+  auto wait_but_last = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kDk16Loads);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- pipeline: step s computes item 2 s + qw on stage s % 3, after requesting item
+  // 2 (s + 2) + qw into stage (s + 2) % 3 (last read in step s - 1, before the barrier
+  // that ended it).  Every step issues the same loads (past the last item through empty
+  // descriptors, which write zeros), so the wait at its end counts exactly.
+  issue(qw, stage_at(0));
+  issue(kDk16Par + qw, stage_at(1));
+#pragma unroll
+  for (int kd = 0; kd < D / 32; ++kd) asm volatile("" : "+v"(kf[kd]), "+v"(vf[kd]));
+  wait_but_last();
+  step_barrier();
+  int st = 0;
+  for (int s = 0; s < n_steps; ++s) {
+    const int st2 = st >= 1 ? st - 1 : st + 2;       // (s + 2) % 3
+    issue(kDk16Par * (s + 2) + qw, stage_at(st2));
+    const int it = kDk16Par * s + qw;
+    if (it < n_items) compute(it, stage_at(st));
+    wait_but_last();
+    step_barrier();
+    st = st == 2 ? 0 : st + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);               // no load into LDS is left in flight
+  step_barrier();
+
+  // ---- add the parities' partial sums (parities 1 .. kDk16Par - 1 one after another
+  // into parity 0's registers), then write dK = scale dK^T^T and dV
+  float* red = reinterpret_cast<float*>(lds);       // [kq][dk | dv][db][j][lane]
+  for (int src = 1; src < kDk16Par; ++src) {
+    if (qw == src) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          red[(((kq * 2 + 0) * (D / 16) + db) * 4 + j) * 64 + lane] = dkacc[db][j];
+          red[(((kq * 2 + 1) * (D / 16) + db) * 4 + j) * 64 + lane] = dvacc[db][j];
+        }
+    }
+    lds_barrier();
+    if (qw == 0) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dkacc[db][j] += red[(((kq * 2 + 0) * (D / 16) + db) * 4 + j) * 64 + lane];
+          dvacc[db][j] += red[(((kq * 2 + 1) * (D / 16) + db) * 4 + j) * 64 + lane];
+        }
+    }
+    lds_barrier();
+  }
+  if (qw == 0 && key < p.T) {
+    const size_t obase = ((size_t)(b * p.h_kv + g) * p.T + key) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      float kk[4], vv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kk[j] = dkacc[db][j] * p.scale;
+        vv[j] = dvacc[db][j];
+      }
+      const int d0 = db * 16 + 4 * G;
+      *reinterpret_cast<float4*>(p.dk + obase + d0) = make_float4(kk[0], kk[1], kk[2], kk[3]);
+      *reinterpret_cast<float4*>(p.dv + obase + d0) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int D>
 struct DqLds {
   static constexpr int KTS = D * 2 + 32;           // K tile: read as rows and transposed
@@ -398,13 +694,6 @@ struct DqLds {
   static_assert(K_BYTES % 1024 == 0 && (kDqTile * VTS) % 1024 == 0, "stages are whole 1 KiB blocks");
   static_assert(K_BLOCKS >= V_BLOCKS, "the K part is the larger");
 };
-
-// One 16-byte-per-lane buffer load written straight into LDS: lane i's 16 bytes from
-// byte voff + soff of the descriptor's range land at dst + 16 i (dst wave-uniform).
-__device__ __forceinline__ void bwd_load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t voff,
-                                               uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
-}
 
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 2)
@@ -600,13 +889,20 @@ hipError_t launch_t(const BwdParams& prm, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   static std::atomic<unsigned long long> dkdv_allowed{0}, dq_allowed{0};
-  e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>), DkdvLds<D>::TOTAL, dkdv_allowed);
-  if (e != hipSuccess) return e;
   e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dq_kernel<D>), DqLds<D>::TOTAL, dq_allowed);
   if (e != hipSuccess) return e;
   const int n_kb = (prm.T + kKeyBlock - 1) / kKeyBlock;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(prm.B * prm.h_kv * n_kb)), dim3(kBwdThreads),
-                     DkdvLds<D>::TOTAL, s, prm);
+  if constexpr (D == 128) {
+    e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dkdv16_kernel), Dkdv16Lds::TOTAL, dkdv_allowed);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv16_kernel, dim3((unsigned)(prm.B * prm.h_kv * n_kb)), dim3(kDk16Threads),
+                       Dkdv16Lds::TOTAL, s, prm);
+  } else {
+    e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>), DkdvLds<D>::TOTAL, dkdv_allowed);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(prm.B * prm.h_kv * n_kb)), dim3(kBwdThreads),
+                       DkdvLds<D>::TOTAL, s, prm);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long n_dq = (long long)prm.B * prm.h_kv * prm.n_hchunks * prm.n_qblocks;

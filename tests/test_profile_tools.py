@@ -41,7 +41,7 @@ DECODE = "void gqa::(anonymous namespace)::decode16_bf16_kernel<128, false, fals
 COMBINE = "void gqa::(anonymous namespace)::decode_combine_kernel<128, false>(gqa::DecodeParams)"
 ROPE = "void gqa::(anonymous namespace)::rope_heads_kernel<unsigned short, 8>(gqa::(anonymous namespace)::RopeSeg)"
 BWD = ["void gqa::(anonymous namespace)::bwd_delta_vec_kernel<128, false>(gqa::BwdParams)",
-       "void gqa::(anonymous namespace)::bwd_dkdv_kernel<128>(gqa::BwdParams)",
+       "gqa::(anonymous namespace)::bwd_dkdv16_kernel(gqa::BwdParams)",
        "void gqa::(anonymous namespace)::bwd_dq_kernel<128>(gqa::BwdParams)"]
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -99,7 +99,7 @@ def test_write_traffic_scales_and_selects(tmp_path, monkeypatch):
         assert e["hbm_bytes_per_launch"] == e["read"] + e["written"]
     assert len(t["rows"]["prefill_causal_bf16_T4096_backward"]["kernels"]) == 3
     md = (prof / "hbm_traffic_counters.md").read_text()
-    assert "gqa::bwd_dkdv_kernel<128>" in md and "copyBuffer" not in md.split("| bench row")[1]
+    assert "gqa::bwd_dkdv16_kernel" in md and "copyBuffer" not in md.split("| bench row")[1]
 
 
 def test_measured_traffic_requires_matching_source(tmp_path, monkeypatch):
