@@ -58,7 +58,7 @@ TRAFFIC_ROWS = {
     "prefill_causal_bf16_T4096_qk_rope": (["--only", "rope"], ("rope_heads_kernel", "largest_grid"),
                                           ["rope.hip", "rope_common.h", "internal.h"]),
     "prefill_causal_bf16_T4096_backward": (["--only", "backward"],
-                                           (("bwd_delta", "bwd_dkdv", "bwd_dq_kernel"), "sum_of_means"),
+                                           (("bwd_dkdv", "bwd_dq_kernel"), "sum_of_means"),
                                            ["backward_bf16.hip", *_COMMON]),
 }
 COPY_ROW = (["--only", "copy"], ("copyBuffer", "mean"))
@@ -476,7 +476,7 @@ def bench_backward(steps, warmup):
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic(w.name + "_backward")},
-            "kernels": "delta + dK/dV + dQ (traffic: the three kernels' bytes summed)", "grad_dtype": "fp32"}
+            "kernels": "dQ (with delta) + dK/dV (traffic: the two kernels' bytes summed)", "grad_dtype": "fp32"}
 
 
 # ---------------------------------------------------------------------------------------- rotary encoding

@@ -30,7 +30,9 @@
 //     reach LDS through buffer loads that write it directly (double-buffered,
 //     the next tile requested as a tile's work starts), each worked in two 32-key
 //     halves (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T) so that two
-//     workgroups fit a CU.
+//     workgroups fit a CU.  It also forms delta for its rows (each row lives in
+//     exactly one dQ workgroup) and stores it, so it runs first and the dK/dV
+//     kernel reads delta from there.
 #include <type_traits>
 
 #include "internal.h"
@@ -58,6 +60,7 @@ struct BwdParams {
   float* dv;
   const int32_t* kv_lens;
   int B, h_q, h_kv, r, T, causal, o_bf16;
+  int dq_delta;            // the dQ kernel forms delta from its own rows (O 16-byte aligned) and stores it
   int hp, P, n_qblocks, n_hchunks;   // dQ row packing (as the forward)
   float scale, c;                    // c = scale * log2(e)
 };
@@ -72,7 +75,8 @@ __device__ __forceinline__ void dkdv_item(int it, int g, int r, int per_head, in
 }
 
 // ---------------------------------------------------------------------------
-// delta_i = sum_d dO_id O_id: one wave per row
+// delta_i = sum_d dO_id O_id, one wave per row with element loads: the pass for an O
+// that is not 16-byte aligned (otherwise the dQ kernel forms delta from its rows)
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_delta_kernel(BwdParams p) {
@@ -89,42 +93,6 @@ bwd_delta_kernel(BwdParams p) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane == 0) p.delta[row] = acc;
-}
-
-// The same with 16-byte loads (O 16-byte aligned): D / 8 lanes per row, 8 values each.
-template <int D, bool O_BF16>
-__global__ void __launch_bounds__(256)
-bwd_delta_vec_kernel(BwdParams p) {
-  constexpr int TPR = D / 8;                   // lanes per row (divides 64)
-  constexpr int RPB = 256 / TPR;               // rows per workgroup
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int part = threadIdx.x % TPR;
-  const long long n_rows = (long long)p.B * p.h_q * p.T;
-  float acc = 0.f;
-  if (row < n_rows) {
-    const size_t base = (size_t)row * D + part * 8;
-    const uint4 dv = *reinterpret_cast<const uint4*>(p.d_o + base);
-    float o[8];
-    if constexpr (O_BF16) {
-      const uint4 ov = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.o) + base);
-      const uint32_t w[4] = {ov.x, ov.y, ov.z, ov.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { o[2 * j] = __uint_as_float(w[j] << 16); o[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u); }
-    } else {
-      const float4 a = reinterpret_cast<const float4*>(static_cast<const float*>(p.o) + base)[0];
-      const float4 b = reinterpret_cast<const float4*>(static_cast<const float*>(p.o) + base)[1];
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-    }
-    const uint32_t w[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf(__uint_as_float(w[j] << 16), o[2 * j], acc);
-      acc = fmaf(__uint_as_float(w[j] & 0xffff0000u), o[2 * j + 1], acc);
-    }
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < n_rows && part == 0) p.delta[row] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -734,7 +702,34 @@ bwd_dq_kernel(BwdParams p) {
     of[kd] = __builtin_bit_cast(bf16x8, y);
   }
   const float lrow = row_valid ? p.lse[rrow] : -INFINITY;
-  const float drow = row_valid ? p.delta[rrow] : 0.f;
+  float drow = 0.f;
+  if (p.dq_delta) {
+    // delta = sum_d dO O for this row: each lane of the pair holds the d values
+    // 16 kd + 8 h .. + 7 of dO in of[kd]; O's matching 8 values come from memory
+    if (row_valid) {
+#pragma unroll
+      for (int kd = 0; kd < D / 16; ++kd) {
+        float o8[8];
+        const size_t e0 = rrow * D + kd * 16 + h * 8;
+        if (p.o_bf16) {
+          const uint4 ov = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.o) + e0);
+          const uint32_t w[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { o8[2 * j] = __uint_as_float(w[j] << 16); o8[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u); }
+        } else {
+          const float4 a = reinterpret_cast<const float4*>(static_cast<const float*>(p.o) + e0)[0];
+          const float4 c = reinterpret_cast<const float4*>(static_cast<const float*>(p.o) + e0)[1];
+          o8[0] = a.x; o8[1] = a.y; o8[2] = a.z; o8[3] = a.w; o8[4] = c.x; o8[5] = c.y; o8[6] = c.z; o8[7] = c.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) drow = fmaf((float)of[kd][j], o8[j], drow);
+      }
+    }
+    drow = pair_sum(drow);
+    if (row_valid && h == 0) p.delta[rrow] = drow;
+  } else if (row_valid) {
+    drow = p.delta[rrow];
+  }
   // a row outside the sequence, or one that sees no key, has L = -inf; its exp2
   // arguments are then made -inf so that all of its P are 0
   const float lc = lrow != -INFINITY ? lrow * kLog2e : INFINITY;
@@ -875,21 +870,25 @@ bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D>
-hipError_t launch_t(const BwdParams& prm, hipStream_t s) {
+hipError_t launch_t(BwdParams prm, hipStream_t s) {
   const long long rows = (long long)prm.B * prm.h_q * prm.T;
-  if (reinterpret_cast<uintptr_t>(prm.o) % 16 == 0) {
-    constexpr int RPB = 256 / (D / 8);
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-    if (prm.o_bf16) hipLaunchKernelGGL((bwd_delta_vec_kernel<D, true>), grid, dim3(256), 0, s, prm);
-    else hipLaunchKernelGGL((bwd_delta_vec_kernel<D, false>), grid, dim3(256), 0, s, prm);
-  } else {
+  // With O 16-byte aligned the dQ kernel forms delta from its rows and runs first; the
+  // dK/dV kernel, which reads delta for every row of its items, follows it.  Otherwise
+  // a separate pass computes delta with element loads before both.
+  prm.dq_delta = reinterpret_cast<uintptr_t>(prm.o) % 16 == 0 ? 1 : 0;
+  hipError_t e = hipSuccess;
+  if (!prm.dq_delta) {
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
 
   static std::atomic<unsigned long long> dkdv_allowed{0}, dq_allowed{0};
   e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dq_kernel<D>), DqLds<D>::TOTAL, dq_allowed);
+  if (e != hipSuccess) return e;
+  const long long n_dq = (long long)prm.B * prm.h_kv * prm.n_hchunks * prm.n_qblocks;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(kBwdThreads), DqLds<D>::TOTAL, s, prm);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_kb = (prm.T + kKeyBlock - 1) / kKeyBlock;
   if constexpr (D == 128) {
@@ -903,10 +902,6 @@ hipError_t launch_t(const BwdParams& prm, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(prm.B * prm.h_kv * n_kb)), dim3(kBwdThreads),
                        DkdvLds<D>::TOTAL, s, prm);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long long n_dq = (long long)prm.B * prm.h_kv * prm.n_hchunks * prm.n_qblocks;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(kBwdThreads), DqLds<D>::TOTAL, s, prm);
   return hipGetLastError();
 }
 

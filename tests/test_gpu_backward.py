@@ -81,6 +81,9 @@ BWD_CASES = [
     (1, 4, 4, 33, 128, True, None),             # MHA
     (1, 2, 1, 1, 64, True, None),               # one row
     (1, 16, 2, 300, 128, True, None),           # r = 8, several key blocks and ragged tail
+    (1, 32, 1, 130, 128, True, None),           # MQA, causal: 32 heads share each key block's items
+    (2, 8, 4, 180, 128, False, [180, 70]),      # no causal mask, padded second sequence
+    (1, 8, 2, 161, 128, True, [100]),           # keys end inside a 64-key block; rows past them see 100 keys
 ]
 
 
@@ -187,3 +190,22 @@ def test_backward_with_o_not_16_byte_aligned(o_dtype):
     want = _oracle(x, d_out, True)
     for name, g, w in zip(("dq", "dk", "dv"), grads, want):
         _check_grad(to_host64(g), w, f"misaligned O {o_dtype} {name}")
+
+
+def test_backward_empty_and_short_sequences():
+    """A sequence with no keys has no visible pair: all of its gradients are 0.  The
+    others (one shorter than a 64-key block) match the oracle one sequence at a time."""
+    B, h_q, h_kv, T, d = 3, 8, 2, 200, 128
+    lens = [200, 0, 45]
+    print(f"case backward lengths {lens}", flush=True)
+    x, d_out, _, got = _run(B, h_q, h_kv, T, d, True, 14900, kv_lens=lens)
+    for b in range(B):
+        if lens[b] == 0:
+            for name, g in zip(("dq", "dk", "dv"), got):
+                assert np.all(g[b] == 0.0), f"empty sequence {name}"
+            continue
+        sl = slice(b, b + 1)
+        xb = {k_: x[k_][sl] for k_ in ("q", "k", "v")}
+        want = _oracle(xb, d_out[sl], True, [lens[b]])
+        for name, g, w in zip(("dq", "dk", "dv"), got, want):
+            _check_grad(g[sl], w, f"lengths {lens} b={b} {name}")

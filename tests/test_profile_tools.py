@@ -40,8 +40,7 @@ PREFILL = "void gqa::(anonymous namespace)::prefill_bf16_kernel<128, false, fals
 DECODE = "void gqa::(anonymous namespace)::decode16_bf16_kernel<128, false, false>(gqa::DecodeParams)"
 COMBINE = "void gqa::(anonymous namespace)::decode_combine_kernel<128, false>(gqa::DecodeParams)"
 ROPE = "void gqa::(anonymous namespace)::rope_heads_kernel<unsigned short, 8>(gqa::(anonymous namespace)::RopeSeg)"
-BWD = ["void gqa::(anonymous namespace)::bwd_delta_vec_kernel<128, false>(gqa::BwdParams)",
-       "gqa::(anonymous namespace)::bwd_dkdv16_kernel(gqa::BwdParams)",
+BWD = ["gqa::(anonymous namespace)::bwd_dkdv16_kernel(gqa::BwdParams)",
        "void gqa::(anonymous namespace)::bwd_dq_kernel<128>(gqa::BwdParams)"]
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -54,8 +53,8 @@ def _fake_runs(out, fetch_scale=2.0):
         if row == "copy":
             disp = [(COPY, 512, (1 << 30) / 1024 / scale)] * 2
         elif row.endswith("_backward"):
-            disp = [(BWD[0], 10, 100.0), (BWD[1], 10, 2000.0), (BWD[2], 10, 3000.0)] * 2
-            want[(counter, row)] = (100.0 + 2000.0 + 3000.0) * 1024 * scale
+            disp = [(BWD[0], 10, 2000.0), (BWD[1], 10, 3000.0)] * 2
+            want[(counter, row)] = (2000.0 + 3000.0) * 1024 * scale
         elif row.endswith("_qk_rope"):
             # the fused Q+K launch has the largest grid; the Q-only launch must not count
             disp = [(ROPE, 1310720, 40.0), (ROPE, 1048576, 32.0), (PREFILL, 262144, 999.0)]
@@ -97,7 +96,7 @@ def test_write_traffic_scales_and_selects(tmp_path, monkeypatch):
         assert e["read"] == round(want[("FETCH_SIZE", row)])
         assert e["written"] == round(want[("WRITE_SIZE", row)])
         assert e["hbm_bytes_per_launch"] == e["read"] + e["written"]
-    assert len(t["rows"]["prefill_causal_bf16_T4096_backward"]["kernels"]) == 3
+    assert len(t["rows"]["prefill_causal_bf16_T4096_backward"]["kernels"]) == 2
     md = (prof / "hbm_traffic_counters.md").read_text()
     assert "gqa::bwd_dkdv16_kernel" in md and "copyBuffer" not in md.split("| bench row")[1]
 
