@@ -25,12 +25,11 @@
 //     add their partial sums at the end.  Head width 128 runs 16 keys per wave on
 //     16x16x32 products, three waves per SIMD (bwd_dkdv16_kernel); head width 64
 //     runs 32 keys per wave on 32x32x16 products, one wave per SIMD.
-//   dQ: a workgroup owns 128 query rows (heads x positions of one group, as in
-//     the forward); Q and dO rows stay in registers and 64-key tiles of K and V
-//     reach LDS through buffer loads that write it directly (double-buffered,
-//     the next tile requested as a tile's work starts), each worked in two 32-key
-//     halves (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T) so that two
-//     workgroups fit a CU.  It also forms delta for its rows (each row lives in
+//   dQ: a workgroup owns 256 query rows (heads x positions of one group, as in
+//     the forward), 32 per wave; Q and dO rows stay in registers and 64-key tiles
+//     of K and V reach LDS through buffer loads that write it directly
+//     (double-buffered, the next tile requested as a tile's work starts), each
+//     worked in two 32-key halves (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T).  It also forms delta for its rows (each row lives in
 //     exactly one dQ workgroup) and stores it, so it runs first and the dK/dV
 //     kernel reads delta from there.
 #include <type_traits>
@@ -44,7 +43,8 @@ namespace {
 constexpr int kBwdThreads = 256;   // 4 waves
 constexpr int kKeyBlock = 64;      // keys per dK/dV workgroup
 constexpr int kQTile = 32;         // query rows per dK/dV tile
-constexpr int kDqRows = 128;       // query rows per dQ workgroup
+constexpr int kDqRows = 256;       // query rows per dQ workgroup
+constexpr int kDqThreads = 512;    // 8 waves of 32 rows
 constexpr int kDqTile = 64;        // keys per dQ tile
 
 struct BwdParams {
@@ -658,13 +658,13 @@ struct DqLds {
   static constexpr int TOTAL = 2 * STAGE;
   static constexpr int K_BLOCKS = K_BYTES / 1024;                  // 1 KiB load blocks per stage
   static constexpr int V_BLOCKS = kDqTile * VTS / 1024;
-  static constexpr int MAXB = (K_BLOCKS + 3) / 4;                  // blocks per wave and tensor
+  static constexpr int MAXB = (K_BLOCKS + 7) / 8;                  // blocks per wave and tensor
   static_assert(K_BYTES % 1024 == 0 && (kDqTile * VTS) % 1024 == 0, "stages are whole 1 KiB blocks");
   static_assert(K_BLOCKS >= V_BLOCKS, "the K part is the larger");
 };
 
 template <int D>
-__global__ void __launch_bounds__(kBwdThreads, 2)
+__global__ void __launch_bounds__(kDqThreads, 1)
 bwd_dq_kernel(BwdParams p) {
   using L = DqLds<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -753,14 +753,14 @@ bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_base, slice);
   // ---- staging: K and V tiles straight from memory into their stages with buffer
   // loads that write LDS directly.  1 KiB block j of a stage's K (V) part is written by
-  // wave j % 4; *_off[i] is this lane's byte offset within a tile for block wave + 4 i.
+  // wave j % 8; *_off[i] is this lane's byte offset within a tile for block wave + 8 i.
   // Keys at or past kv_end read as zeros (the descriptors' range ends there); a lane
   // whose 16 bytes are row padding reads at 2^31, outside any range the API admits, so
   // it touches no memory and writes zeros into padding no product reads.
   uint32_t k_off[L::MAXB], v_off[L::MAXB];
 #pragma unroll
   for (int i = 0; i < L::MAXB; ++i) {
-    const int a = (wave + 4 * i) * 1024 + lane * 16;
+    const int a = (wave + 8 * i) * 1024 + lane * 16;
     const int rk = a / L::KTS, ok = a - rk * L::KTS;
     const int rv = a / L::VTS, ov = a - rv * L::VTS;
     k_off[i] = ok < D * 2 ? (uint32_t)(rk * D * 2 + ok) : 0x80000000u;
@@ -770,9 +770,9 @@ bwd_dq_kernel(BwdParams p) {
     const uint32_t soff = (uint32_t)t * kDqTile * D * 2;
 #pragma unroll
     for (int i = 0; i < L::MAXB; ++i) {
-      if (wave + 4 * i < L::K_BLOCKS) bwd_load_lds16(krs, stage + (wave + 4 * i) * 1024, k_off[i], soff);
-      if (wave + 4 * i < L::V_BLOCKS)
-        bwd_load_lds16(vrs, stage + L::K_BYTES + (wave + 4 * i) * 1024, v_off[i], soff);
+      if (wave + 8 * i < L::K_BLOCKS) bwd_load_lds16(krs, stage + (wave + 8 * i) * 1024, k_off[i], soff);
+      if (wave + 8 * i < L::V_BLOCKS)
+        bwd_load_lds16(vrs, stage + L::K_BYTES + (wave + 8 * i) * 1024, v_off[i], soff);
     }
   };
   auto wait_loads = []() __attribute__((always_inline)) {
@@ -887,7 +887,7 @@ hipError_t launch_t(BwdParams prm, hipStream_t s) {
   e = allow_dynamic_lds(reinterpret_cast<const void*>(bwd_dq_kernel<D>), DqLds<D>::TOTAL, dq_allowed);
   if (e != hipSuccess) return e;
   const long long n_dq = (long long)prm.B * prm.h_kv * prm.n_hchunks * prm.n_qblocks;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(kBwdThreads), DqLds<D>::TOTAL, s, prm);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(kDqThreads), DqLds<D>::TOTAL, s, prm);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_kb = (prm.T + kKeyBlock - 1) / kKeyBlock;
