@@ -30,7 +30,7 @@ ABS_MAX = 2e-2
 ABS_MEAN = 2e-3
 
 
-def _check_grad(got, want, what):
+def _check_grad(got, want, what, absolute=True):
     assert got.shape == want.shape
     assert np.all(np.isfinite(got)), f"{what}: non-finite"
     nrm = np.linalg.norm(want)
@@ -49,8 +49,9 @@ def _check_grad(got, want, what):
     assert mx <= MAX_REL, f"{what}: max error {mx:.3g} of max |g|"
     # the forward's absolute bar (2e-2 max-abs, 2e-3 mean-abs) for gradients of unit
     # scale; larger gradients carry the same bar relative to their scale
-    assert abs_max <= ABS_MAX * max(1.0, g_max), f"{what}: max-abs {abs_max:.3g}"
-    assert abs_mean <= ABS_MEAN * max(1.0, g_mean), f"{what}: mean-abs {abs_mean:.3g}"
+    if absolute:
+        assert abs_max <= ABS_MAX * max(1.0, g_max), f"{what}: max-abs {abs_max:.3g}"
+        assert abs_mean <= ABS_MEAN * max(1.0, g_mean), f"{what}: mean-abs {abs_mean:.3g}"
 
 
 def _run(B, h_q, h_kv, T, d, causal, seed, kv_lens=None, out_dtype="f32"):
@@ -130,13 +131,17 @@ def test_backward_deterministic_and_key_gradients_sum_to_zero():
     assert np.max(np.abs(dk.sum(axis=2))) <= 1e-3 * np.max(np.abs(dk)) * np.sqrt(dk.shape[2])
 
 
-def test_backward_prefill_workload_sampled():
-    """The causal prefill workload at full size: dQ rows and the gradients of the
-    last keys (seen by few rows) against the oracle; the key-gradient sum at all keys."""
+def test_backward_prefill_workload_every_element():
+    """The causal prefill workload at full size (B=1, h_q=32, h_kv=8, d_h=128, T=4096),
+    in the launch configuration the benchmark times: every element of dQ, dK and dV
+    against the float64 oracle, one K/V head's group of query heads per host thread,
+    under the bar above for each gradient of each group; rows at tile edges on their own."""
     import torch
 
+    from tests.gpu_util import parallel_map
+
     w = inputs.WORKLOADS["prefill_causal_bf16_T4096"]
-    print(f"case {w.name} backward", flush=True)
+    print(f"case {w.name} backward, every element", flush=True)
     x = inputs.make_workload(w)
     d_out = inputs.normal(w.seed, "d_out", (w.B, w.h_q, w.T, w.d_h), "bf16")
     q, k, v, do = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(d_out, "bf16")
@@ -144,27 +149,30 @@ def test_backward_prefill_workload_sampled():
     dq, dk, dv = ops.gqa_prefill_backward(q, k, v, o, do, lse)
     torch.cuda.synchronize()
     dq, dk, dv = to_host64(dq), to_host64(dk), to_host64(dv)
+    del q, k, v, do, o, lse
     r = w.h_q // w.h_kv
-    Q, K, V, DO = (f64(a, "bf16") for a in (x["q"], x["k"], x["v"], d_out))
-    # dQ of sampled rows: the oracle on one query row at its position against its K/V head
-    for a in (0, 5, 31):
-        g = a // r
-        for i in (0, 1, 63, 64, 2047, 4095):
-            want = oracle.attention_backward(Q[:, a:a + 1, i:i + 1], K[:, g:g + 1, : i + 1], V[:, g:g + 1, : i + 1],
-                                             DO[:, a:a + 1, i:i + 1], causal=True, q_pos=np.array([[i]]))[0]
-            got = dq[0, a, i]
-            # + 1e-4: row 0 has one key, so dP - delta cancels to fp32 rounding (exact answer 0)
-            assert np.linalg.norm(got - want[0, 0, 0]) <= REL_FRO * np.linalg.norm(want) + 1e-4, (a, i)
-    # dK, dV of the last 64 keys of two K/V heads: only rows >= T - 64 see them, so the oracle
-    # on those rows of the group's r heads gives their whole gradient
-    lo = w.T - 64
-    for g in (0, 7):
-        _, dkw, dvw = oracle.attention_backward(Q[:, g * r:(g + 1) * r, lo:], K[:, g:g + 1], V[:, g:g + 1],
-                                                DO[:, g * r:(g + 1) * r, lo:], causal=True,
-                                                q_pos=np.arange(lo, w.T)[None, :])
-        _check_grad(dk[0, g, lo:], dkw[0, 0, lo:], f"full-size dK tail g={g}")
-        _check_grad(dv[0, g, lo:], dvw[0, 0, lo:], f"full-size dV tail g={g}")
-    assert np.max(np.abs(dk.sum(axis=2))) <= 1e-3 * np.max(np.abs(dk)) * np.sqrt(w.T)
+
+    def group(g):
+        hs = slice(g * r, (g + 1) * r)
+        return oracle.attention_backward(f64(x["q"][:, hs], "bf16"), f64(x["k"][:, g:g + 1], "bf16"),
+                                         f64(x["v"][:, g:g + 1], "bf16"), f64(d_out[:, hs], "bf16"), causal=True)
+
+    wants = parallel_map(group, range(w.h_kv))
+    for g, (wq, wk, wv) in enumerate(wants):
+        hs = slice(g * r, (g + 1) * r)
+        _check_grad(dq[:, hs], wq, f"full-size dQ g={g}")
+        _check_grad(dk[:, g:g + 1], wk, f"full-size dK g={g}")
+        _check_grad(dv[:, g:g + 1], wv, f"full-size dV g={g}")
+        # tile edges of the query rows (dQ; row 0 sees one key, so its exact dQ is 0 and
+        # the whole-tensor check above covers it) and of the keys (dK, dV: 16-, 32- and
+        # 64-key blocks), each row under the relative bars: a row of an early key sums
+        # ~16K rounded terms, so its error sits at the 2^-9-scale relative level and the
+        # absolute mean bar, derived for whole tensors, does not apply to it
+        for i in (1, 15, 16, 31, 32, 63, 64, 2047, 2048, 4095):
+            _check_grad(dq[:, hs, i], wq[:, :, i], f"full-size dQ g={g} row {i}", absolute=False)
+        for j in (0, 1, 15, 16, 31, 32, 63, 64, 2047, 2048, 4095):
+            _check_grad(dk[:, g, j], wk[:, 0, j], f"full-size dK g={g} key {j}", absolute=False)
+            _check_grad(dv[:, g, j], wv[:, 0, j], f"full-size dV g={g} key {j}", absolute=False)
 
 
 @pytest.mark.parametrize("o_dtype", ["f32", "bf16"])
